@@ -1,0 +1,154 @@
+/*
+ * matopt.h - C ABI of libmatopt.so: the owner-local Muon step and the Sign-Muon
+ * tail on one AMD Instinct MI355X (gfx950), in hand-written HIP kernels.
+ *
+ * Sources (web pages, cited by title and section):
+ *   "Riassunto Tecnico: MatrixFSDP" (gist.science, paper 2607.05895),
+ *     "Metodologia: MatrixFSDP", item 1 (owner-shaped placement): one owner rank
+ *     holds each 2D weight matrix whole and, after the gradient reduction, runs the
+ *     Newton-Schulz update on it locally with no matrix communication.  The list of
+ *     whole matrices one owner holds is the batch these calls take.
+ *   "Riepilogo Tecnico: SignMuon" (gist.science, paper 2605.16311), section 2:
+ *     momentum -> Newton-Schulz polar direction -> elementwise sign -> 1-bit
+ *     packing -> integer-sum majority vote with a sign threshold.
+ *
+ * Readings where the pages are silent (stated once here, used throughout):
+ *   momentum      M <- beta*M + G (heavy-ball, one fp32 buffer), one fused
+ *                 multiply-add per element;
+ *   scaling       X0 = M / (||M||_F + eps), per matrix;
+ *   iteration     X <- a X + (b A + c A^2) X with A = X X^T, applied `iters` times
+ *                 on the orientation with rows <= cols (a tall matrix is processed
+ *                 as its transpose and the result is returned in the caller's
+ *                 orientation);
+ *   sign          bit = (u >= 0): +0 and -0 give +1, NaN gives -1;
+ *   bit layout    flat row-major element i -> word i/32, bit i%32 (LSB first),
+ *                 1 means +1, unused bits of the last word are 0;
+ *   vote          sum_i = 2*count_i - M, out bit = (sum_i >= 0): ties give +1.
+ *
+ * Conventions for every call:
+ *   - All buffer pointers are DEVICE pointers on the current HIP device, owned by
+ *     the caller.  The library allocates no device memory on these calls; scratch
+ *     comes from the caller's `workspace` (size from muon_workspace_bytes).  The
+ *     only library-owned memory is a small pinned host staging ring for the
+ *     per-call descriptor table, created on first use.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and the
+ *     call returns without waiting for the GPU.  `mats` is read before return.
+ *   - Return value 0 (MO_OK) or a negative MO_ERR_* code.  Argument errors are
+ *     found on the host before anything is launched; mo_last_error() then returns
+ *     a message (thread-local).  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MATOPT_H
+#define MATOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MATOPT_VERSION 100
+
+/* element types */
+enum { MO_F32 = 0, MO_BF16 = 1 };
+
+/* return codes */
+enum {
+  MO_OK = 0,
+  MO_ERR_INVALID = -1,     /* bad shape, null pointer, bad scalar, bad count       */
+  MO_ERR_UNSUPPORTED = -2, /* dtype combination not provided                       */
+  MO_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required      */
+  MO_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed           */
+};
+
+/* Newton-Schulz parameters: the quintic coefficients, the step count (>= 0; 0
+ * returns the Frobenius-scaled input) and the epsilon of the scaling. */
+typedef struct {
+  float a, b, c;
+  int32_t iters;
+  float eps;
+} mo_ns_params;
+
+/* One owned matrix: rows x cols, row-major, contiguous (leading dimension = cols).
+ * rows, cols >= 1.  Unused pointers may be NULL. */
+typedef struct {
+  int64_t rows, cols;
+  const void *grad;  /* muon_step_batched: gradient, rows*cols of grad_dtype        */
+  float *momentum;   /* muon_step_batched: fp32 momentum, updated in place          */
+  const void *x;     /* ns_orthogonalize: input, rows*cols of in_dtype              */
+  void *out;         /* both: the orthogonalised U, rows*cols of out_dtype          */
+} mo_matrix;
+
+/* Bytes of device workspace muon_step_batched / ns_orthogonalize need for this
+ * list with this compute dtype (MO_F32 or MO_BF16).  Returns 0 if the list is
+ * invalid (then mo_last_error() says why).  The workspace holds, per matrix, the
+ * iterate X and two copies of X^T (ping-pong), A and B, each padded to multiples
+ * of 256 in both dimensions, plus the per-call descriptor table and the per-matrix
+ * norm partial sums. */
+size_t muon_workspace_bytes(const mo_matrix *mats, int32_t count, int32_t compute_dtype);
+
+/* The owner-local Muon step on `count` matrices, batched: for each matrix
+ *   M <- beta*M + G            (fp32, in place)
+ *   X <- M / (||M||_F + eps)   (oriented so that rows <= cols)
+ *   repeat ns->iters times: A = X X^T; B = b A + c A A; X <- a X + B X
+ *   out <- X                   (caller's orientation, out_dtype)
+ * grad_dtype: MO_F32 or MO_BF16.  compute_dtype: MO_F32 (fp32 operands) or MO_BF16
+ * (bf16 operands X, A, B with fp32 accumulation; A and B are rounded to bf16 once
+ * and b*A + c*A^2 is formed from the same rounded A).  out_dtype: MO_F32 or MO_BF16.
+ * out must not overlap grad or momentum.  Deterministic: identical inputs give
+ * bit-identical outputs, and a matrix's result does not depend on the rest of
+ * the batch. */
+int32_t muon_step_batched(const mo_matrix *mats, int32_t count, int32_t grad_dtype,
+                          int32_t compute_dtype, int32_t out_dtype, float beta,
+                          const mo_ns_params *ns, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Frobenius scaling and Newton-Schulz only (no momentum): out <- NS(x / (||x|| + eps)).
+ * in_dtype: MO_F32 or MO_BF16.  x == out is allowed. */
+int32_t ns_orthogonalize(const mo_matrix *mats, int32_t count, int32_t in_dtype,
+                         int32_t compute_dtype, int32_t out_dtype, const mo_ns_params *ns,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Elementwise sign and 1-bit packing ("Riepilogo Tecnico: SignMuon", section 2,
+ * core mechanism item 2 and distributed flow items 2-3; "Efficienza di
+ * Comunicazione": one bit per element).  u: numel values of dtype (MO_F32 or
+ * MO_BF16) in flat order; packed: ceil(numel/32) uint32 words (written whole,
+ * pad bits 0).  numel >= 1. */
+int32_t sign_pack(const void *u, int32_t dtype, int64_t numel, uint32_t *packed, void *stream);
+
+/* Majority vote over M packed sign buffers ("Riepilogo Tecnico: SignMuon",
+ * section 2, core mechanism item 3 and distributed flow item 4: integer sum of the
+ * signs, then a sign threshold).  packed: [M][ceil(numel/32)] uint32, worker-major
+ * (the layout an all-gather of packed buffers produces).  out_packed:
+ * ceil(numel/32) words, bit = (sum >= 0), pad bits 0.  out_sum: NULL, or numel
+ * int8 values sum_i = 2*count_i - M (needs M <= 127).  1 <= M <= 65535. */
+int32_t sign_vote(const uint32_t *packed, int32_t M, int64_t numel, uint32_t *out_packed,
+                  int8_t *out_sum, void *stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *mo_last_error(void);
+
+/* MATOPT_VERSION of the built library. */
+int32_t mo_version(void);
+
+/* Per-kernel timing for measurement.  mo_profile_begin() makes the calls above
+ * record a HIP event pair around every kernel they launch (on the call's stream);
+ * mo_profile_end() waits for those events and fills up to `max` records, one per
+ * kernel kind, returning how many kinds were seen (or a negative code).
+ * Profiling state is process-wide; the calls are not thread-safe. */
+typedef struct {
+  char name[32];     /* kernel kind, e.g. "ns_syrk"                               */
+  int64_t launches;  /* launches recorded                                          */
+  double total_ms;   /* sum of event-measured durations                            */
+} mo_kernel_time;
+
+int32_t mo_profile_begin(void);
+int32_t mo_profile_end(mo_kernel_time *out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MATOPT_H */

@@ -17,4 +17,9 @@ from .binding import (  # noqa: F401
     sign_vote,
     workspace_bytes,
     version,
+    profile_begin,
+    profile_end,
+    Workspace,
+    MO_F32,
+    MO_BF16,
 )

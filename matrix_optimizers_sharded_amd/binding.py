@@ -1,13 +1,257 @@
-"""ctypes binding over libmatopt.so (placeholder until the library exists)."""
+"""ctypes binding over libmatopt.so (C ABI in include/matopt.h).
+
+Argument marshalling only: tensors are passed as raw device pointers with torch's
+current stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: a missing library or a failed call raises MatoptError.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+MO_F32, MO_BF16 = 0, 1
+ERRORS = {-1: "MO_ERR_INVALID", -2: "MO_ERR_UNSUPPORTED", -3: "MO_ERR_WORKSPACE", -4: "MO_ERR_HIP"}
 
 
 class MatoptError(RuntimeError):
-    pass
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
 
 
-def _missing(*_a, **_k):
-    raise MatoptError("libmatopt.so is not built")
+class MoMatrix(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p), ("x", ctypes.c_void_p), ("out", ctypes.c_void_p)]
 
 
-load_library = library_path = muon_step_batched = ns_orthogonalize = _missing
-sign_pack = sign_vote = workspace_bytes = version = _missing
+class MoNsParams(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
+                ("iters", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class MoKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def library_path():
+    return os.environ.get("MATOPT_LIB", os.path.join(PKG, "lib", "libmatopt.so"))
+
+
+def load_library():
+    """Load libmatopt.so (raises MatoptError if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise MatoptError(-4, f"{path} not found; build it with python -m matrix_optimizers_sharded_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.muon_workspace_bytes.argtypes = [ctypes.POINTER(MoMatrix), I32, I32]
+    lib.muon_workspace_bytes.restype = SZ
+    lib.muon_step_batched.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32, F,
+                                      ctypes.POINTER(MoNsParams), P, SZ, P]
+    lib.muon_step_batched.restype = I32
+    lib.ns_orthogonalize.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32,
+                                     ctypes.POINTER(MoNsParams), P, SZ, P]
+    lib.ns_orthogonalize.restype = I32
+    lib.sign_pack.argtypes = [P, I32, I64, P, P]
+    lib.sign_pack.restype = I32
+    lib.sign_vote.argtypes = [P, I32, I64, P, P, P]
+    lib.sign_vote.restype = I32
+    lib.mo_last_error.argtypes = []
+    lib.mo_last_error.restype = ctypes.c_char_p
+    lib.mo_version.argtypes = []
+    lib.mo_version.restype = I32
+    lib.mo_profile_begin.argtypes = []
+    lib.mo_profile_begin.restype = I32
+    lib.mo_profile_end.argtypes = [ctypes.POINTER(MoKernelTime), I32]
+    lib.mo_profile_end.restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        msg = _lib.mo_last_error().decode(errors="replace")
+        raise MatoptError(rc, msg)
+    return rc
+
+
+def version():
+    return load_library().mo_version()
+
+
+def _dtype_code(dt):
+    import torch
+    if dt == torch.float32:
+        return MO_F32
+    if dt == torch.bfloat16:
+        return MO_BF16
+    raise MatoptError(-2, f"unsupported dtype {dt}")
+
+
+def _stream_ptr(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _mats(shapes, grads=None, moms=None, xs=None, outs=None):
+    arr = (MoMatrix * max(len(shapes), 1))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i].rows, arr[i].cols = int(r), int(c)
+        if grads is not None:
+            arr[i].grad = grads[i].data_ptr()
+        if moms is not None:
+            arr[i].momentum = moms[i].data_ptr()
+        if xs is not None:
+            arr[i].x = xs[i].data_ptr()
+        if outs is not None:
+            arr[i].out = outs[i].data_ptr()
+    return arr
+
+
+def workspace_bytes(shapes, compute):
+    """Workspace bytes for a list of (rows, cols) with compute dtype torch.float32 or
+    torch.bfloat16."""
+    lib = load_library()
+    n = lib.muon_workspace_bytes(_mats(shapes), len(shapes), _dtype_code(compute))
+    if n == 0 and len(shapes) > 0:
+        raise MatoptError(-1, lib.mo_last_error().decode())
+    return n
+
+
+class Workspace:
+    """Device scratch for the batched calls, grown on demand (torch allocation)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        import torch
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = None
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def _validate(ts, shapes, name, dtypes=None):
+    for t, (r, c) in zip(ts, shapes):
+        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (r, c):
+            raise MatoptError(-1, f"{name}: expected a contiguous CUDA tensor of shape {(r, c)}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise MatoptError(-2, f"{name}: unsupported dtype {t.dtype}")
+
+
+def _ns_params(a, b, c, iters, eps):
+    return MoNsParams(float(a), float(b), float(c), int(iters), float(eps))
+
+
+def muon_step_batched(grads, moms, outs, beta, a, b, c, iters, eps=1e-7, compute=None,
+                      workspace=None):
+    """In place: moms[i] <- beta*moms[i] + grads[i]; outs[i] <- NS_k(moms[i] / (||.||+eps)).
+
+    grads: list of fp32 or bf16 tensors (one dtype); moms: fp32; outs: fp32 or bf16
+    (one dtype); compute: torch.float32 or torch.bfloat16 (bf16 operands, fp32
+    accumulation).  workspace: a Workspace (one is made per call if None)."""
+    import torch
+    lib = load_library()
+    if compute is None:
+        compute = torch.bfloat16
+    shapes = [tuple(g.shape) for g in grads]
+    if not (len(grads) == len(moms) == len(outs)):
+        raise MatoptError(-1, "grads, moms and outs must have the same length")
+    if not shapes:
+        return
+    _validate(grads, shapes, "grads", (torch.float32, torch.bfloat16))
+    _validate(moms, shapes, "moms", (torch.float32,))
+    _validate(outs, shapes, "outs", (torch.float32, torch.bfloat16))
+    gdt, odt = grads[0].dtype, outs[0].dtype
+    if any(g.dtype != gdt for g in grads) or any(o.dtype != odt for o in outs):
+        raise MatoptError(-2, "all grads (and all outs) must share one dtype")
+    mats = _mats(shapes, grads=grads, moms=moms, outs=outs)
+    nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
+    ws = (workspace or Workspace(grads[0].device)).get(nbytes)
+    ns = _ns_params(a, b, c, iters, eps)
+    _check(lib.muon_step_batched(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute), _dtype_code(odt),
+                                 float(beta), ctypes.byref(ns), ws.data_ptr(), ws.numel(),
+                                 _stream_ptr(grads[0])))
+
+
+def ns_orthogonalize(xs, outs, a, b, c, iters, eps=1e-7, compute=None, workspace=None):
+    """outs[i] <- NS_k(xs[i] / (||xs[i]||_F + eps)); xs[i] may be outs[i] when the
+    dtypes match."""
+    import torch
+    lib = load_library()
+    if compute is None:
+        compute = torch.bfloat16
+    shapes = [tuple(x.shape) for x in xs]
+    if len(xs) != len(outs):
+        raise MatoptError(-1, "xs and outs must have the same length")
+    if not shapes:
+        return
+    _validate(xs, shapes, "xs", (torch.float32, torch.bfloat16))
+    _validate(outs, shapes, "outs", (torch.float32, torch.bfloat16))
+    idt, odt = xs[0].dtype, outs[0].dtype
+    if any(x.dtype != idt for x in xs) or any(o.dtype != odt for o in outs):
+        raise MatoptError(-2, "all xs (and all outs) must share one dtype")
+    mats = _mats(shapes, xs=xs, outs=outs)
+    nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
+    ws = (workspace or Workspace(xs[0].device)).get(nbytes)
+    ns = _ns_params(a, b, c, iters, eps)
+    _check(lib.ns_orthogonalize(mats, len(shapes), _dtype_code(idt), _dtype_code(compute), _dtype_code(odt),
+                                ctypes.byref(ns), ws.data_ptr(), ws.numel(), _stream_ptr(xs[0])))
+
+
+def sign_pack(u, packed=None):
+    """1-bit signs of u (flat order) -> int32 tensor of ceil(numel/32) words (bit
+    patterns of the uint32 words)."""
+    import torch
+    lib = load_library()
+    if not u.is_cuda or not u.is_contiguous():
+        raise MatoptError(-1, "u must be a contiguous CUDA tensor")
+    numel = u.numel()
+    nwords = (numel + 31) // 32
+    if packed is None:
+        packed = torch.empty(nwords, dtype=torch.int32, device=u.device)
+    if packed.numel() < nwords or packed.dtype != torch.int32 or not packed.is_contiguous():
+        raise MatoptError(-1, "packed must be a contiguous int32 tensor of ceil(numel/32) words")
+    _check(lib.sign_pack(u.data_ptr(), _dtype_code(u.dtype), numel, packed.data_ptr(), _stream_ptr(u)))
+    return packed
+
+
+def sign_vote(packed, numel, out_packed=None, with_sums=False):
+    """Majority vote over packed[M][nwords] (int32 tensor).  Returns (out_packed,
+    sums or None)."""
+    import torch
+    lib = load_library()
+    if packed.dim() != 2 or packed.dtype != torch.int32 or not packed.is_contiguous() or not packed.is_cuda:
+        raise MatoptError(-1, "packed must be a contiguous CUDA int32 tensor [M][nwords]")
+    M, nwords = packed.shape
+    if nwords != (numel + 31) // 32:
+        raise MatoptError(-1, "packed width must be ceil(numel/32)")
+    if out_packed is None:
+        out_packed = torch.empty(nwords, dtype=torch.int32, device=packed.device)
+    sums = torch.empty(numel, dtype=torch.int8, device=packed.device) if with_sums else None
+    _check(lib.sign_vote(packed.data_ptr(), M, numel, out_packed.data_ptr(),
+                         sums.data_ptr() if sums is not None else None, _stream_ptr(packed)))
+    return out_packed, sums
+
+
+def profile_begin():
+    _check(load_library().mo_profile_begin())
+
+
+def profile_end():
+    """Per-kernel-kind {name: (launches, total_ms)} since profile_begin()."""
+    lib = load_library()
+    buf = (MoKernelTime * 32)()
+    n = lib.mo_profile_end(buf, 32)
+    if n < 0:
+        _check(n)
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 32))}

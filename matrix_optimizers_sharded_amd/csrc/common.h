@@ -1,0 +1,68 @@
+// Shared device types and the per-matrix descriptor of one batched call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace mo {
+
+// Work decomposition of each batched launch kind.  Every kernel finds its matrix
+// by a binary search of `begin[kind]` over the descriptor table.
+enum Kind {
+  KIND_SYRK = 0,   // upper-triangle 256x256 tiles of A = X X^T
+  KIND_POLY = 1,   // upper-triangle 256x256 tiles of B = bA + cA^2
+  KIND_APPLY = 2,  // 256x256 tiles of X <- aX + BX
+  KIND_PREP = 3,   // 64x64 tiles of the padded oriented X0 (and X0^T)
+  KIND_CHUNK = 4,  // 4096-element chunks of the caller's matrix (momentum, norm)
+  NKIND = 5
+};
+
+constexpr int GEMM_TILE = 256;   // workspace dims are padded to multiples of this
+constexpr int PREP_TILE = 64;
+constexpr int CHUNK = 4096;      // elements per momentum / sum-of-squares block
+
+struct MatDesc {
+  // caller buffers
+  const void* grad;   // gradient (momentum step) or input x (orthogonalise only)
+  float* mom;         // fp32 momentum, null for orthogonalise only
+  void* out;          // U in the caller's orientation
+  int64_t rows, cols, numel;
+  // oriented problem: X is m x n with m = min(rows, cols), n = max(rows, cols)
+  int32_t m, n, mp, np;   // mp, np: m and n rounded up to GEMM_TILE
+  int32_t transposed;     // 1 if rows > cols (X = M^T)
+  int32_t vec_ok;         // 1 if grad/mom/out allow 16-byte vector access
+  // workspace buffers, compute dtype, zero outside the m x n corner
+  void* X;                // mp x np, updated in place by the apply step
+  void* XT[2];            // np x mp, ping-pong (read by apply as its B operand)
+  void* A;                // mp x mp, symmetric
+  void* B;                // mp x mp, symmetric
+  int64_t begin[NKIND];   // first work item of this matrix per launch kind
+  int64_t items[NKIND];   // work items of this matrix per launch kind
+  int32_t scale_slot;     // index into the per-matrix scale array
+  int32_t pad_;
+};
+
+__device__ inline int find_desc(const MatDesc* __restrict__ d, int count, int kind, int64_t item) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (d[mid].begin[kind] <= item) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ inline float bf16_to_f32(bf16_t v) { return static_cast<float>(v); }
+
+template <typename T> __device__ inline T from_f32(float v);
+template <> __device__ inline float from_f32<float>(float v) { return v; }
+template <> __device__ inline bf16_t from_f32<bf16_t>(float v) { return static_cast<bf16_t>(v); }
+
+template <typename T> __device__ inline float to_f32(T v) { return static_cast<float>(v); }
+
+}  // namespace mo

@@ -1,0 +1,260 @@
+// HBM-streaming kernels: the fused momentum + sum-of-squares pass, the per-matrix
+// scale, the scaled/oriented/padded operand writer, and the sign pack / vote.
+#pragma once
+
+#include "common.h"
+
+namespace mo {
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Fixed-order block sum for 256 threads (4 waves); result valid in thread 0.
+template <typename T>
+__device__ inline T block_sum_256(T v) {
+  __shared__ T part[4];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T r = 0;
+  if (threadIdx.x == 0) r = ((part[0] + part[1]) + part[2]) + part[3];
+  return r;
+}
+
+template <typename T> __device__ inline f32x4_t load4_f32(const T* p);
+template <> __device__ inline f32x4_t load4_f32<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <> __device__ inline f32x4_t load4_f32<bf16_t>(const bf16_t* p) {
+  bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+  return f32x4_t{static_cast<float>(v[0]), static_cast<float>(v[1]),
+                 static_cast<float>(v[2]), static_cast<float>(v[3])};
+}
+
+// Pass 1, one 4096-element chunk per block.  With MOMENTUM: M <- fma(beta, M, G)
+// in place, and the chunk's sum of M^2 goes to partial[item].  Without: the sum of
+// squares of the input only.
+template <typename TG, bool MOMENTUM>
+__global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restrict__ descs,
+                                                        int count, float beta,
+                                                        float* __restrict__ partial) {
+  const int64_t item = blockIdx.x;
+  const MatDesc& d = descs[find_desc(descs, count, KIND_CHUNK, item)];
+  const int64_t e0 = (item - d.begin[KIND_CHUNK]) * CHUNK;
+  const int64_t numel = d.numel;
+  const TG* __restrict__ g = static_cast<const TG*>(d.grad);
+  float* __restrict__ m = d.mom;
+  float ss = 0.f;
+  if (d.vec_ok && e0 + CHUNK <= numel) {
+    f32x4_t gv[4], mv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gv[q] = load4_f32<TG>(g + e0 + q * 1024 + threadIdx.x * 4);
+    if (MOMENTUM) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mv[q] = *reinterpret_cast<const f32x4_t*>(m + e0 + q * 1024 + threadIdx.x * 4);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4_t v = gv[q];
+      if (MOMENTUM) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(beta, mv[q][t], gv[q][t]);
+        *reinterpret_cast<f32x4_t*>(m + e0 + q * 1024 + threadIdx.x * 4) = v;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ss = __builtin_fmaf(v[t], v[t], ss);
+    }
+  } else {
+    const int64_t e1 = (e0 + CHUNK < numel) ? e0 + CHUNK : numel;
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+      float v = static_cast<float>(g[e]);
+      if (MOMENTUM) {
+        v = __builtin_fmaf(beta, m[e], v);
+        m[e] = v;
+      }
+      ss = __builtin_fmaf(v, v, ss);
+    }
+  }
+  ss = block_sum_256(ss);
+  if (threadIdx.x == 0) partial[item] = ss;
+}
+
+// One block per matrix: scale = 1 / (sqrt(sum of partials) + eps), summed in fp64
+// in a fixed order.
+__global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ descs,
+                                                    const float* __restrict__ partial,
+                                                    float eps, float* __restrict__ scale) {
+  const MatDesc& d = descs[blockIdx.x];
+  double s = 0.0;
+  const float* p = partial + d.begin[KIND_CHUNK];
+  for (int64_t c = threadIdx.x; c < d.items[KIND_CHUNK]; c += 256) s += static_cast<double>(p[c]);
+  s = block_sum_256(s);
+  if (threadIdx.x == 0) scale[d.scale_slot] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
+}
+
+// Pass 2, one 64x64 tile of the padded oriented operand per block: X = S * scale
+// (S = the updated momentum, or the input), written as X (mp x np) and X^T
+// (np x mp) in the compute dtype, zero outside the m x n corner.  The source tile
+// is read along its contiguous dimension and both outputs are written along theirs,
+// through an LDS tile.
+template <typename TS, typename TC>
+__global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict__ descs, int count,
+                                                      const float* __restrict__ scale,
+                                                      int from_momentum) {
+  __shared__ float tile[PREP_TILE][PREP_TILE + 1];
+  const int64_t item = blockIdx.x;
+  const MatDesc& d = descs[find_desc(descs, count, KIND_PREP, item)];
+  const int64_t local = item - d.begin[KIND_PREP];
+  const int tn = d.np / PREP_TILE;
+  const int i0 = static_cast<int>(local / tn) * PREP_TILE;   // rows of X
+  const int j0 = static_cast<int>(local % tn) * PREP_TILE;   // cols of X
+  const float s = scale[d.scale_slot];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t ld = d.cols;
+  // source rows/cols of this tile: X[i][j] = S[i][j] (not transposed) or S[j][i]
+  const int r0 = d.transposed ? j0 : i0, c0 = d.transposed ? i0 : j0;
+  const int64_t rlim = d.rows, clim = d.cols;
+  const float* sm = d.mom;
+  const TS* sx = static_cast<const TS*>(d.grad);
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int a = ty + 4 * q;
+    const int64_t r = r0 + a, c = c0 + tx;
+    float v = 0.f;
+    if (r < rlim && c < clim) v = from_momentum ? sm[r * ld + c] : static_cast<float>(sx[r * ld + c]);
+    tile[a][tx] = v * s;
+  }
+  __syncthreads();
+  TC* X = static_cast<TC*>(d.X);
+  TC* XT = static_cast<TC*>(d.XT[0]);
+  const int64_t ldx = d.np, ldt = d.mp;
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int a = ty + 4 * q;
+    // X[i0 + a][j0 + tx]
+    const float vx = d.transposed ? tile[tx][a] : tile[a][tx];
+    X[static_cast<int64_t>(i0 + a) * ldx + j0 + tx] = from_f32<TC>(vx);
+    // XT[j0 + a][i0 + tx] = X[i0 + tx][j0 + a]
+    const float vt = d.transposed ? tile[a][tx] : tile[tx][a];
+    XT[static_cast<int64_t>(j0 + a) * ldt + i0 + tx] = from_f32<TC>(vt);
+  }
+}
+
+// iters == 0: out = S * scale in the caller's orientation and out dtype.
+template <typename TS, typename TO>
+__global__ __launch_bounds__(256) void k_scaled_copy(const MatDesc* __restrict__ descs, int count,
+                                                     const float* __restrict__ scale,
+                                                     int from_momentum) {
+  const int64_t item = blockIdx.x;
+  const MatDesc& d = descs[find_desc(descs, count, KIND_CHUNK, item)];
+  const int64_t e0 = (item - d.begin[KIND_CHUNK]) * CHUNK;
+  const int64_t e1 = (e0 + CHUNK < d.numel) ? e0 + CHUNK : d.numel;
+  const float s = scale[d.scale_slot];
+  TO* out = static_cast<TO*>(d.out);
+  const TS* sx = static_cast<const TS*>(d.grad);
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    const float v = from_momentum ? d.mom[e] : static_cast<float>(sx[e]);
+    out[e] = from_f32<TO>(v * s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sign-Muon tail.
+
+// One thread per 8 consecutive elements -> one byte; 4 lanes OR their bytes into
+// a 32-bit word (element i -> bit i % 32 of word i / 32).  bit = (u >= 0).
+template <typename T>
+__global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int64_t numel,
+                                                   uint32_t* __restrict__ packed, int vec_ok) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e0 = t * 8;
+  uint32_t byte = 0;
+  if (vec_ok && e0 + 8 <= numel) {
+    if (sizeof(T) == 4) {
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(u + e0);
+      const f32x4_t x0 = p[0], x1 = p[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        byte |= static_cast<uint32_t>(x0[k] >= 0.f) << k;
+        byte |= static_cast<uint32_t>(x1[k] >= 0.f) << (k + 4);
+      }
+    } else {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(u + e0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) byte |= static_cast<uint32_t>(static_cast<float>(x[k]) >= 0.f) << k;
+    }
+  } else {
+    for (int k = 0; k < 8; ++k) {
+      const int64_t e = e0 + k;
+      if (e < numel) byte |= static_cast<uint32_t>(static_cast<float>(u[e]) >= 0.f) << k;
+    }
+  }
+  const int lane = threadIdx.x & 63;
+  uint32_t w = byte << (8 * (lane & 3));
+  w |= __shfl_xor(w, 1, 64);
+  w |= __shfl_xor(w, 2, 64);
+  const int64_t nwords = (numel + 31) >> 5;
+  if ((lane & 3) == 0 && (t >> 2) < nwords) packed[t >> 2] = w;
+}
+
+// One thread per packed word: a bit-sliced counter adds the M workers' words (all
+// 32 bit positions at once), a bit-sliced compare gives count >= ceil(M/2), which
+// is 2*count - M >= 0 (ties -> +1).  Optionally the int8 sums 2*count - M.
+__global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M,
+                                                   int levels, int64_t numel, int64_t nwords,
+                                                   uint32_t* __restrict__ out,
+                                                   int8_t* __restrict__ out_sum) {
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (w >= nwords) return;
+  uint32_t cnt[16];
+#pragma unroll
+  for (int l = 0; l < 16; ++l) cnt[l] = 0u;
+  for (int k = 0; k < M; ++k) {
+    uint32_t carry = packed[static_cast<int64_t>(k) * nwords + w];
+#pragma unroll
+    for (int l = 0; l < 16; ++l) {
+      if (l < levels) {
+        const uint32_t c = cnt[l];
+        cnt[l] = c ^ carry;
+        carry = c & carry;
+      }
+    }
+  }
+  // count >= T with T = ceil(M/2) <=> carry out of count + (2^levels - T)
+  const uint32_t addend = (1u << levels) - static_cast<uint32_t>((M + 1) >> 1);
+  uint32_t carry = 0u;
+#pragma unroll
+  for (int l = 0; l < 16; ++l) {
+    if (l < levels) {
+      const uint32_t k = ((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u;
+      carry = (cnt[l] & k) | ((cnt[l] ^ k) & carry);
+    }
+  }
+  uint32_t valid = 0xFFFFFFFFu;
+  const int64_t tail = numel - w * 32;
+  if (tail < 32) valid = (1u << tail) - 1u;
+  out[w] = carry & valid;
+  if (out_sum) {
+    const int n = tail < 32 ? static_cast<int>(tail) : 32;
+    int8_t* dst = out_sum + w * 32;
+    for (int b = 0; b < n; ++b) {
+      int c = 0;
+#pragma unroll
+      for (int l = 0; l < 16; ++l)
+        if (l < levels) c |= static_cast<int>((cnt[l] >> b) & 1u) << l;
+      dst[b] = static_cast<int8_t>(2 * c - M);
+    }
+  }
+}
+
+}  // namespace mo

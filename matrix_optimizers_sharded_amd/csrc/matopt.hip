@@ -1,0 +1,429 @@
+// libmatopt: host side of the C ABI declared in include/matopt.h.
+//
+// One batched call = one descriptor table (uploaded to the head of the caller's
+// workspace through a pinned staging ring) + a fixed launch sequence on the
+// caller's stream:
+//   k_momentum_sumsq   momentum fma in place + per-chunk sum of squares  (HBM)
+//   k_norm_scale       per-matrix 1 / (||M||_F + eps)                    (tiny)
+//   k_prep_operand     scaled, oriented, zero-padded X0 and X0^T         (HBM)
+//   iters x { k_ns_gemm<SYRK>, k_ns_gemm<POLY>, k_ns_gemm<APPLY> }       (MFMA)
+// Each launch covers every matrix of the batch (grouped launch); blocks find their
+// matrix by binary search over the table, which is sorted by decreasing size so
+// the longest tiles start first.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/matopt.h"
+#include "common.h"
+#include "elementwise.h"
+#include "gemm.h"
+
+using namespace mo;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+size_t dtype_size(int dt) { return dt == MO_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == MO_F32 || dt == MO_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  std::vector<MatDesc> descs;
+  int64_t total[NKIND] = {0, 0, 0, 0, 0};
+  size_t off_desc = 0, off_scale = 0, off_partial = 0, bytes = 0;
+};
+
+// Validate the list and lay out the workspace.  base == nullptr only sizes it.
+int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, unsigned char* base,
+               Plan& plan, int in_dtype = MO_F32, int out_dtype = MO_F32) {
+  if (count < 0) return fail(MO_ERR_INVALID, "count must be >= 0");
+  if (count > 0 && !mats) return fail(MO_ERR_INVALID, "mats is NULL");
+  if (!valid_dtype(compute)) return fail(MO_ERR_UNSUPPORTED, "compute dtype must be MO_F32 or MO_BF16");
+  const size_t es = dtype_size(compute);
+  std::vector<int> order(count);
+  std::iota(order.begin(), order.end(), 0);
+  for (int i = 0; i < count; ++i) {
+    const mo_matrix& mt = mats[i];
+    if (mt.rows < 1 || mt.cols < 1 || mt.rows > MAX_DIM || mt.cols > MAX_DIM)
+      return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": rows and cols must be in [1, 2^24]");
+    if (base) {
+      if (!mt.out) return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": out is NULL");
+      if (momentum && (!mt.grad || !mt.momentum))
+        return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": grad or momentum is NULL");
+      if (!momentum && !mt.x) return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": x is NULL");
+      if (!momentum && mt.x == mt.out && in_dtype != out_dtype)
+        return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": x == out needs in_dtype == out_dtype");
+    }
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int p, int q) {
+    return mats[p].rows * mats[p].cols > mats[q].rows * mats[q].cols;
+  });
+  size_t off = 0;
+  plan.off_desc = off;
+  off = align_up(off + sizeof(MatDesc) * std::max(count, 1), ALIGN);
+  plan.off_scale = off;
+  off = align_up(off + sizeof(float) * std::max(count, 1), ALIGN);
+  int64_t chunks = 0;
+  for (int i = 0; i < count; ++i) chunks += (mats[i].rows * mats[i].cols + CHUNK - 1) / CHUNK;
+  plan.off_partial = off;
+  off = align_up(off + sizeof(float) * std::max<int64_t>(chunks, 1), ALIGN);
+
+  plan.descs.resize(count);
+  for (int k = 0; k < count; ++k) {
+    const mo_matrix& mt = mats[order[k]];
+    MatDesc& d = plan.descs[k];
+    std::memset(&d, 0, sizeof(d));
+    d.grad = momentum ? mt.grad : mt.x;
+    d.mom = momentum ? mt.momentum : nullptr;
+    d.out = mt.out;
+    d.rows = mt.rows;
+    d.cols = mt.cols;
+    d.numel = mt.rows * mt.cols;
+    d.transposed = mt.rows > mt.cols ? 1 : 0;
+    d.m = static_cast<int32_t>(std::min(mt.rows, mt.cols));
+    d.n = static_cast<int32_t>(std::max(mt.rows, mt.cols));
+    d.mp = static_cast<int32_t>(round_up(d.m, GEMM_TILE));
+    d.np = static_cast<int32_t>(round_up(d.n, GEMM_TILE));
+    d.vec_ok = (aligned16(d.grad) && aligned16(d.mom) && aligned16(d.out) && (mt.cols % 4 == 0)) ? 1 : 0;
+    d.scale_slot = k;
+    const size_t xb = size_t(d.mp) * size_t(d.np) * es, ab = size_t(d.mp) * size_t(d.mp) * es;
+    auto take = [&](size_t nb) {
+      void* p = base ? static_cast<void*>(base + off) : nullptr;
+      off = align_up(off + nb, ALIGN);
+      return p;
+    };
+    d.X = take(xb);
+    d.XT[0] = take(xb);
+    d.XT[1] = take(xb);
+    d.A = take(ab);
+    d.B = take(ab);
+    const int64_t tm = d.mp / GEMM_TILE, tn = d.np / GEMM_TILE;
+    d.items[KIND_SYRK] = tm * (tm + 1) / 2;
+    d.items[KIND_POLY] = tm * (tm + 1) / 2;
+    d.items[KIND_APPLY] = tm * tn;
+    d.items[KIND_PREP] = (int64_t(d.mp) / PREP_TILE) * (int64_t(d.np) / PREP_TILE);
+    d.items[KIND_CHUNK] = (d.numel + CHUNK - 1) / CHUNK;
+    for (int kd = 0; kd < NKIND; ++kd) {
+      d.begin[kd] = plan.total[kd];
+      plan.total[kd] += d.items[kd];
+    }
+  }
+  for (int kd = 0; kd < NKIND; ++kd)
+    if (plan.total[kd] > 0x7fffffffLL) return fail(MO_ERR_INVALID, "batch too large for one launch");
+  plan.bytes = off;
+  return MO_OK;
+}
+
+// ---- pinned staging ring for descriptor uploads --------------------------------
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+std::mutex g_stage_mu;
+StagingSlot g_ring[4];
+int g_ring_next = 0;
+
+int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  StagingSlot& s = g_ring[g_ring_next];
+  g_ring_next = (g_ring_next + 1) % 4;
+  if (s.pending) {
+    if (hipEventSynchronize(s.ev) != hipSuccess) return fail(MO_ERR_HIP, "staging event wait failed");
+    s.pending = false;
+  }
+  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
+    return fail(MO_ERR_HIP, "hipEventCreate failed");
+  if (s.cap < bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(align_up(bytes, 4096), 65536);
+    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(MO_ERR_HIP, "hipHostMalloc of the staging buffer failed");
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return fail(MO_ERR_HIP, "descriptor upload failed");
+  if (hipEventRecord(s.ev, stream) != hipSuccess) return fail(MO_ERR_HIP, "hipEventRecord failed");
+  s.pending = true;
+  return MO_OK;
+}
+
+// ---- optional per-kernel timing ------------------------------------------------
+struct ProfRec {
+  int kind;
+  hipEvent_t e0, e1;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_ev_pool;
+const char* const kKindNames[] = {"momentum_sumsq", "norm_scale", "prep_operand", "scaled_copy",
+                                  "ns_syrk", "ns_poly", "ns_apply", "sign_pack", "sign_vote"};
+enum { PK_MOM = 0, PK_SCALE, PK_PREP, PK_COPY, PK_SYRK, PK_POLY, PK_APPLY, PK_PACK, PK_VOTE, PK_N };
+
+hipEvent_t take_event() {
+  if (!g_ev_pool.empty()) {
+    hipEvent_t e = g_ev_pool.back();
+    g_ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  (void)hipEventCreate(&e);
+  return e;
+}
+
+// Launch helper: optional event bracket + launch error check.
+template <typename F>
+int launch(int pk, hipStream_t stream, F&& f) {
+  ProfRec rec{pk, nullptr, nullptr};
+  if (g_prof) {
+    rec.e0 = take_event();
+    rec.e1 = take_event();
+    (void)hipEventRecord(rec.e0, stream);
+  }
+  f();
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(MO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
+  if (g_prof) {
+    (void)hipEventRecord(rec.e1, stream);
+    g_prof_recs.push_back(rec);
+  }
+  return MO_OK;
+}
+
+#define MO_TRY(x)            \
+  do {                       \
+    int rc_ = (x);           \
+    if (rc_ != MO_OK) return rc_; \
+  } while (0)
+
+template <typename T, typename TO>
+int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, hipStream_t stream) {
+  for (int t = 0; t < ns.iters; ++t) {
+    const int parity = t & 1;
+    MO_TRY(launch(PK_SYRK, stream, [&] {
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(plan.total[KIND_SYRK]), dim3(256), 0, stream,
+                         dd, count, parity, 0.f, 0.f, 0.f);
+    }));
+    MO_TRY(launch(PK_POLY, stream, [&] {
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(plan.total[KIND_POLY]), dim3(256), 0, stream,
+                         dd, count, parity, 0.f, ns.b, ns.c);
+    }));
+    const bool last = (t + 1 == ns.iters);
+    MO_TRY(launch(PK_APPLY, stream, [&] {
+      if (last)
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(plan.total[KIND_APPLY]), dim3(256), 0,
+                           stream, dd, count, parity, ns.a, 0.f, 0.f);
+      else
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(plan.total[KIND_APPLY]), dim3(256), 0, stream,
+                           dd, count, parity, ns.a, 0.f, 0.f);
+    }));
+  }
+  return MO_OK;
+}
+
+template <typename TS, typename TC, typename TO>
+int run_after_scale(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
+                    const mo_ns_params& ns, hipStream_t stream) {
+  const int from_mom = momentum ? 1 : 0;
+  if (ns.iters == 0) {
+    return launch(PK_COPY, stream, [&] {
+      hipLaunchKernelGGL((k_scaled_copy<TS, TO>), dim3(plan.total[KIND_CHUNK]), dim3(256), 0, stream, dd,
+                         count, scale, from_mom);
+    });
+  }
+  MO_TRY(launch(PK_PREP, stream, [&] {
+    hipLaunchKernelGGL((k_prep_operand<TS, TC>), dim3(plan.total[KIND_PREP]), dim3(256), 0, stream, dd,
+                       count, scale, from_mom);
+  }));
+  return run_ns<TC, TO>(dd, count, plan, ns, stream);
+}
+
+template <typename TS>
+int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
+                         int compute, int out, const mo_ns_params& ns, hipStream_t stream) {
+  if (compute == MO_BF16) {
+    if (out == MO_BF16) return run_after_scale<TS, bf16_t, bf16_t>(dd, count, plan, scale, momentum, ns, stream);
+    return run_after_scale<TS, bf16_t, float>(dd, count, plan, scale, momentum, ns, stream);
+  }
+  if (out == MO_BF16) return run_after_scale<TS, float, bf16_t>(dd, count, plan, scale, momentum, ns, stream);
+  return run_after_scale<TS, float, float>(dd, count, plan, scale, momentum, ns, stream);
+}
+
+int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out, bool momentum, float beta,
+            const mo_ns_params* ns, void* workspace, size_t ws_bytes, void* stream_ptr) {
+  g_err.clear();
+  if (!ns) return fail(MO_ERR_INVALID, "ns params is NULL");
+  if (!valid_dtype(in_dtype) || !valid_dtype(compute) || !valid_dtype(out))
+    return fail(MO_ERR_UNSUPPORTED, "dtypes must be MO_F32 or MO_BF16");
+  if (ns->iters < 0) return fail(MO_ERR_INVALID, "iters must be >= 0");
+  if (!std::isfinite(ns->a) || !std::isfinite(ns->b) || !std::isfinite(ns->c) || !std::isfinite(ns->eps) ||
+      ns->eps < 0.f || !std::isfinite(beta))
+    return fail(MO_ERR_INVALID, "coefficients, beta and eps must be finite, eps >= 0");
+  Plan plan;
+  MO_TRY(build_plan(mats, count, compute, momentum, nullptr, plan, in_dtype, out));
+  if (count == 0) return MO_OK;
+  if (!workspace) return fail(MO_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(workspace) & (ALIGN - 1)))
+    return fail(MO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < plan.bytes)
+    return fail(MO_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.bytes) + " bytes");
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  Plan full;
+  MO_TRY(build_plan(mats, count, compute, momentum, base, full, in_dtype, out));
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  MatDesc* dd = reinterpret_cast<MatDesc*>(base + full.off_desc);
+  float* scale = reinterpret_cast<float*>(base + full.off_scale);
+  float* partial = reinterpret_cast<float*>(base + full.off_partial);
+  MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
+
+  MO_TRY(launch(PK_MOM, stream, [&] {
+    const dim3 grid(full.total[KIND_CHUNK]);
+    if (momentum) {
+      if (in_dtype == MO_BF16)
+        hipLaunchKernelGGL((k_momentum_sumsq<bf16_t, true>), grid, dim3(256), 0, stream, dd, count, beta, partial);
+      else
+        hipLaunchKernelGGL((k_momentum_sumsq<float, true>), grid, dim3(256), 0, stream, dd, count, beta, partial);
+    } else {
+      if (in_dtype == MO_BF16)
+        hipLaunchKernelGGL((k_momentum_sumsq<bf16_t, false>), grid, dim3(256), 0, stream, dd, count, beta, partial);
+      else
+        hipLaunchKernelGGL((k_momentum_sumsq<float, false>), grid, dim3(256), 0, stream, dd, count, beta, partial);
+    }
+  }));
+  MO_TRY(launch(PK_SCALE, stream, [&] {
+    hipLaunchKernelGGL(k_norm_scale, dim3(count), dim3(256), 0, stream, dd, partial, ns->eps, scale);
+  }));
+  // after the momentum step the NS source is the fp32 momentum; otherwise the input
+  if (momentum || in_dtype == MO_F32)
+    return dispatch_compute_out<float>(dd, count, full, scale, momentum, compute, out, *ns, stream);
+  return dispatch_compute_out<bf16_t>(dd, count, full, scale, momentum, compute, out, *ns, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_workspace_bytes(const mo_matrix* mats, int32_t count, int32_t compute_dtype) {
+  g_err.clear();
+  Plan plan;
+  if (build_plan(mats, count, compute_dtype, true, nullptr, plan) != MO_OK) return 0;
+  return plan.bytes;
+}
+
+int32_t muon_step_batched(const mo_matrix* mats, int32_t count, int32_t grad_dtype, int32_t compute_dtype,
+                          int32_t out_dtype, float beta, const mo_ns_params* ns, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return batched(mats, count, grad_dtype, compute_dtype, out_dtype, true, beta, ns, workspace, workspace_bytes,
+                 stream);
+}
+
+int32_t ns_orthogonalize(const mo_matrix* mats, int32_t count, int32_t in_dtype, int32_t compute_dtype,
+                         int32_t out_dtype, const mo_ns_params* ns, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return batched(mats, count, in_dtype, compute_dtype, out_dtype, false, 0.f, ns, workspace, workspace_bytes,
+                 stream);
+}
+
+int32_t sign_pack(const void* u, int32_t dtype, int64_t numel, uint32_t* packed, void* stream_ptr) {
+  g_err.clear();
+  if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
+  if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
+  if (!u || !packed) return fail(MO_ERR_INVALID, "u or packed is NULL");
+  const int64_t threads = ((numel + 31) / 32) * 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int vec = aligned16(u) ? 1 : 0;
+  return launch(PK_PACK, stream, [&] {
+    if (dtype == MO_F32)
+      hipLaunchKernelGGL((k_sign_pack<float>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const float*>(u), numel, packed, vec);
+    else
+      hipLaunchKernelGGL((k_sign_pack<bf16_t>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const bf16_t*>(u), numel, packed, vec);
+  });
+}
+
+int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* out_packed, int8_t* out_sum,
+                  void* stream_ptr) {
+  g_err.clear();
+  if (M < 1 || M > 65535) return fail(MO_ERR_INVALID, "M must be in [1, 65535]");
+  if (out_sum && M > 127) return fail(MO_ERR_INVALID, "int8 sums need M <= 127");
+  if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
+  if (!packed || !out_packed) return fail(MO_ERR_INVALID, "packed or out_packed is NULL");
+  const int64_t nwords = (numel + 31) / 32;
+  const int64_t blocks = (nwords + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
+  int levels = 0;
+  while ((1 << levels) <= M) ++levels;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  return launch(PK_VOTE, stream, [&] {
+    hipLaunchKernelGGL(k_sign_vote, dim3(blocks), dim3(256), 0, stream, packed, M, levels, numel, nwords,
+                       out_packed, out_sum);
+  });
+}
+
+const char* mo_last_error(void) { return g_err.c_str(); }
+
+int32_t mo_version(void) { return MATOPT_VERSION; }
+
+int32_t mo_profile_begin(void) {
+  g_prof = true;
+  return MO_OK;
+}
+
+int32_t mo_profile_end(mo_kernel_time* out, int32_t max) {
+  g_err.clear();
+  g_prof = false;
+  double ms[PK_N] = {0};
+  int64_t n[PK_N] = {0};
+  int rc = MO_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess)
+      rc = fail(MO_ERR_HIP, "event timing failed");
+    ms[r.kind] += t;
+    n[r.kind] += 1;
+    g_ev_pool.push_back(r.e0);
+    g_ev_pool.push_back(r.e1);
+  }
+  g_prof_recs.clear();
+  if (rc != MO_OK) return rc;
+  int k = 0;
+  for (int i = 0; i < PK_N; ++i) {
+    if (!n[i]) continue;
+    if (out && k < max) {
+      std::memset(&out[k], 0, sizeof(mo_kernel_time));
+      std::strncpy(out[k].name, kKindNames[i], sizeof(out[k].name) - 1);
+      out[k].launches = n[i];
+      out[k].total_ms = ms[i];
+    }
+    ++k;
+  }
+  return k;
+}
+
+}  // extern "C"

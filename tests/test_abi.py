@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from matrix_optimizers_sharded_amd import binding
+from matrix_optimizers_sharded_amd.binding import MoMatrix, MoNsParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "matopt.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libmatopt.so is not built (python -m matrix_optimizers_sharded_amd.build)")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("muon_step_batched", "ns_orthogonalize", "sign_pack", "sign_vote"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    text = open(HEADER).read()
+    assert lib.mo_version() == int(re.search(r"#define MATOPT_VERSION (\d+)", text).group(1))
+
+
+def mats(*shapes):
+    arr = (MoMatrix * len(shapes))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i].rows, arr[i].cols = r, c
+    return arr
+
+
+def test_workspace_bytes_grows_with_padded_shapes(lib):
+    one = lib.muon_workspace_bytes(mats((256, 256)), 1, binding.MO_BF16)
+    # X, X^T x2, A, B at 256x256 bf16 = 5 * 128 KiB, plus tables
+    assert 5 * 256 * 256 * 2 <= one < 5 * 256 * 256 * 2 + 8192
+    # a 1x1 matrix pads to 256x256
+    assert lib.muon_workspace_bytes(mats((1, 1)), 1, binding.MO_BF16) == one
+    assert lib.muon_workspace_bytes(mats((256, 256)), 1, binding.MO_F32) > one
+    two = lib.muon_workspace_bytes(mats((256, 256), (300, 700)), 2, binding.MO_BF16)
+    assert two > one
+    assert lib.muon_workspace_bytes(mats((0, 5)), 1, binding.MO_BF16) == 0
+    assert b"rows and cols" in lib.mo_last_error()
+
+
+def test_invalid_arguments_fail_before_launch(lib):
+    ns = MoNsParams(3.4445, -4.775, 2.0315, 5, 1e-7)
+    fake = ctypes.c_void_p(0x1000)
+    m = mats((4, 4))
+    m[0].grad, m[0].momentum, m[0].out = 0x1000, 0x1000, 0x2000
+    # negative iteration count
+    bad = MoNsParams(1, 1, 1, -1, 1e-7)
+    assert lib.muon_step_batched(m, 1, 1, 1, 1, 0.9, ctypes.byref(bad), fake, 1 << 20, None) == -1
+    # unsupported dtype code
+    assert lib.muon_step_batched(m, 1, 7, 1, 1, 0.9, ctypes.byref(ns), fake, 1 << 20, None) == -2
+    # workspace too small / missing
+    assert lib.muon_step_batched(m, 1, 1, 1, 1, 0.9, ctypes.byref(ns), fake, 16, None) == -3
+    assert b"workspace too small" in lib.mo_last_error()
+    assert lib.muon_step_batched(m, 1, 1, 1, 1, 0.9, ctypes.byref(ns), None, 1 << 20, None) == -3
+    # missing gradient pointer
+    m[0].grad = None
+    assert lib.muon_step_batched(m, 1, 1, 1, 1, 0.9, ctypes.byref(ns), ctypes.c_void_p(0x100000),
+                                 1 << 20, None) == -1
+    # non-finite coefficient
+    nan = MoNsParams(float("nan"), 1, 1, 1, 1e-7)
+    assert lib.ns_orthogonalize(m, 1, 1, 1, 1, ctypes.byref(nan), fake, 1 << 20, None) == -1
+    # x == out with different dtypes
+    m2 = mats((4, 4))
+    m2[0].x, m2[0].out = 0x100000, 0x100000
+    assert lib.ns_orthogonalize(m2, 1, 1, 1, 0, ctypes.byref(ns), ctypes.c_void_p(0x200000),
+                                1 << 20, None) == -1
+    # count == 0 is a no-op
+    assert lib.muon_step_batched(m, 0, 1, 1, 1, 0.9, ctypes.byref(ns), None, 0, None) == 0
+    # sign calls
+    assert lib.sign_pack(fake, 1, 0, fake, None) == -1
+    assert lib.sign_pack(fake, 5, 10, fake, None) == -2
+    assert lib.sign_pack(None, 1, 10, fake, None) == -1
+    assert lib.sign_vote(fake, 0, 10, fake, None, None) == -1
+    assert lib.sign_vote(fake, 70000, 10, fake, None, None) == -1
+    assert lib.sign_vote(fake, 128, 10, fake, fake, None) == -1
+    assert b"M <= 127" in lib.mo_last_error()
+    assert lib.sign_vote(fake, 3, 0, fake, None, None) == -1
+
+
+def test_profile_without_launches_is_empty(lib):
+    assert lib.mo_profile_begin() == 0
+    assert lib.mo_profile_end(None, 0) == 0

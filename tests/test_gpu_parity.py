@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by
+element, on seeded inputs.  Bars: fp32 compute <= 1e-4 and bf16 compute <= 2e-2
+relative Frobenius error per matrix; momentum state and all integer stages
+bit-exact."""
+
+import numpy as np
+import pytest
+
+import oracle
+from matrix_optimizers_sharded_amd.workloads import (
+    MUON_ABC, TEXTBOOK_QUINTIC_ABC, BETA, EPS, WORKLOADS, host_matrix)
+from gpu_util import (say, to_dev_f32, to_dev_bf16, host_f32, rel_err, gaussian, bf16_round,
+                      run_muon, run_ns)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def tdt(name):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+# ---------------------------------------------------------------- sign tail
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("numel", [1, 7, 31, 32, 33, 64, 100, 1000, 4099, 65536 + 13])
+def test_sign_pack_bit_exact(gpu, dtype, numel):
+    import torch
+    from matrix_optimizers_sharded_amd import sign_pack
+    say(f"sign_pack dtype={dtype} numel={numel}")
+    rng = np.random.default_rng(numel)
+    v = rng.standard_normal(numel).astype(np.float32)
+    v[rng.random(numel) < 0.05] = 0.0
+    v[rng.random(numel) < 0.05] = -0.0
+    if numel > 10:
+        v[3] = np.nan
+    if dtype == "bf16":
+        bits, vals = bf16_round(np.nan_to_num(v, nan=0.0))
+        vals = vals.copy()
+        u = to_dev_bf16(bits, gpu)
+    else:
+        vals = v
+        u = to_dev_f32(v, gpu)
+    packed = sign_pack(u)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got, oracle.sign_pack(host_f32(u)))
+
+
+def test_sign_pack_unaligned_view(gpu):
+    import torch
+    from matrix_optimizers_sharded_amd import sign_pack
+    v = gaussian(1001, 3)
+    u = to_dev_f32(v, gpu)[1:]          # 4-byte offset: scalar load path
+    packed = sign_pack(u)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), oracle.sign_pack(v[1:]))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 127])
+@pytest.mark.parametrize("numel", [1, 33, 1000, 65537])
+def test_sign_vote_bit_exact(gpu, M, numel):
+    import torch
+    from matrix_optimizers_sharded_amd import sign_vote
+    say(f"sign_vote M={M} numel={numel}")
+    rng = np.random.default_rng(M * 7 + numel)
+    packed = np.stack([oracle.sign_pack(rng.standard_normal(numel)) for _ in range(M)])
+    dev = torch.from_numpy(packed.view(np.int32)).to(gpu)
+    out, sums = sign_vote(dev, numel, with_sums=True)
+    torch.cuda.synchronize()
+    want_out, want_sums = oracle.majority_vote(packed, numel)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want_out)
+    np.testing.assert_array_equal(sums.cpu().numpy().astype(np.int64), want_sums)
+
+
+def test_sign_vote_large_M_without_sums(gpu):
+    import torch
+    from matrix_optimizers_sharded_amd import sign_vote
+    M, numel = 1000, 777
+    rng = np.random.default_rng(1)
+    packed = rng.integers(0, 2 ** 32, size=(M, (numel + 31) // 32), dtype=np.uint64).astype(np.uint32)
+    packed[:, -1] &= np.uint32((1 << (numel % 32)) - 1)
+    out, _ = sign_vote(torch.from_numpy(packed.view(np.int32)).to(gpu), numel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), oracle.majority_vote(packed, numel)[0])
+
+
+# ---------------------------------------------------------------- Muon step
+
+def check_muon(grads, moms, got_m, got_u, compute, abc, iters, beta=BETA, eps=EPS, label=""):
+    worst = 0.0
+    for i, (g, m0, gm, gu) in enumerate(zip(grads, moms, got_m, got_u)):
+        want_m, want_u = oracle.muon_step(g, m0, beta, *abc, iters, eps)
+        np.testing.assert_array_equal(gm.view(np.uint32), want_m.view(np.uint32),
+                                      err_msg=f"{label} matrix {i}: momentum state")
+        e = rel_err(gu, want_u)
+        worst = max(worst, e)
+        assert e <= TOL[compute], f"{label} matrix {i} shape {g.shape}: rel err {e:.3e}"
+    say(f"{label}: worst rel err {worst:.3e}")
+    return worst
+
+
+def test_single_256x128_fp32(gpu):
+    import torch
+    w = WORKLOADS[1]
+    inp = host_matrix(1, 0)
+    say("workload single-256x128 fp32")
+    gm, gu = run_muon(gpu, [inp["grad"]], [inp["mom"]], torch.float32, torch.float32, torch.float32,
+                      BETA, MUON_ABC, w.iters, EPS)
+    check_muon([inp["grad"]], [inp["mom"]], gm, gu, "f32", MUON_ABC, w.iters, label="single-256x128")
+
+
+RAGGED = [(1, 1), (1, 300), (300, 1), (257, 129), (129, 257), (300, 200), (512, 512), (700, 260), (64, 1000)]
+
+
+@pytest.mark.parametrize("compute", ["f32", "bf16"])
+@pytest.mark.parametrize("iters", [0, 1, 5])
+def test_ragged_shapes(gpu, compute, iters):
+    import torch
+    say(f"ragged shapes compute={compute} iters={iters}")
+    grads = [gaussian(s, 100 + i) for i, s in enumerate(RAGGED)]
+    moms = [gaussian(s, 200 + i) for i, s in enumerate(RAGGED)]
+    gm, gu = run_muon(gpu, grads, moms, torch.float32, tdt(compute), torch.float32, BETA, MUON_ABC, iters, EPS)
+    check_muon(grads, moms, gm, gu, compute, MUON_ABC, iters, label=f"ragged {compute} k={iters}")
+
+
+@pytest.mark.parametrize("compute", ["f32", "bf16"])
+def test_ns_orthogonalize_and_out_dtypes(gpu, compute):
+    import torch
+    shapes = [(96, 320), (320, 96), (256, 256)]
+    xs = [gaussian(s, 300 + i, 0.05) for i, s in enumerate(shapes)]
+    for in_dt, out_dt in [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")]:
+        say(f"ns_orthogonalize compute={compute} in={in_dt} out={out_dt}")
+        xin = [bf16_round(x)[1] for x in xs] if in_dt == "bf16" else xs
+        got = run_ns(gpu, xin, tdt(in_dt), tdt(compute), tdt(out_dt), MUON_ABC, 5, EPS)
+        tol = TOL[compute] if out_dt == "f32" else max(TOL[compute], 2e-2)
+        for x, u in zip(xin, got):
+            e = rel_err(u, oracle.ns_orthogonalize(x, *MUON_ABC, 5, EPS))
+            assert e <= tol, (in_dt, out_dt, x.shape, e)
+
+
+def test_ns_in_place(gpu):
+    import torch
+    from matrix_optimizers_sharded_amd import ns_orthogonalize
+    x = gaussian((200, 600), 9)
+    t = to_dev_f32(x, gpu)
+    ns_orthogonalize([t], [t], *MUON_ABC, 3, EPS, compute=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_err(host_f32(t), oracle.ns_orthogonalize(x, *MUON_ABC, 3, EPS)) <= 1e-4
+
+
+def test_textbook_quintic_bf16(gpu):
+    import torch
+    shapes = [(512, 768), (768, 512)]
+    grads = [gaussian(s, 400 + i, 0.02) for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 500 + i, 0.02) for i, s in enumerate(shapes)]
+    gm, gu = run_muon(gpu, grads, moms, torch.float32, torch.bfloat16, torch.float32, BETA,
+                      TEXTBOOK_QUINTIC_ABC, 5, EPS)
+    worst = check_muon(grads, moms, gm, gu, "bf16", TEXTBOOK_QUINTIC_ABC, 5, label="textbook quintic bf16")
+    assert worst < 5e-3
+
+
+def test_zero_matrix_gives_zero(gpu):
+    import torch
+    z = np.zeros((300, 500), np.float32)
+    for compute in (torch.float32, torch.bfloat16):
+        gm, gu = run_muon(gpu, [z], [z], torch.float32, compute, torch.float32, BETA, MUON_ABC, 5, EPS)
+        assert np.all(gu[0] == 0) and np.all(gm[0] == 0)
+
+
+def _workload_inputs(wid):
+    ins = [host_matrix(wid, i) for i in range(WORKLOADS[wid].count)]
+    return [d["grad"] for d in ins], [d["mom"] for d in ins]
+
+
+def test_125m_class_owner_set_bf16(gpu):
+    """All 72 matrices of the 125M-class owner set in one batched call."""
+    import torch
+    w = WORKLOADS[2]
+    say("workload 125m-class, 72 matrices, bf16 grads, bf16 compute")
+    grads, moms = _workload_inputs(2)
+    gm, gu = run_muon(gpu, grads, moms, torch.bfloat16, torch.bfloat16, torch.bfloat16, BETA, MUON_ABC,
+                      w.iters, EPS)
+    check_muon(grads, moms, gm, gu, "bf16", MUON_ABC, w.iters, label="125m-class")
+
+
+def test_125m_class_fp32_grads_fp32_compute(gpu):
+    import torch
+    w = WORKLOADS[2]
+    grads, moms = _workload_inputs(2)
+    idx = [0, 4, 5]
+    grads, moms = [grads[i] for i in idx], [moms[i] for i in idx]
+    gm, gu = run_muon(gpu, grads, moms, torch.float32, torch.float32, torch.float32, BETA, MUON_ABC,
+                      w.iters, EPS)
+    check_muon(grads, moms, gm, gu, "f32", MUON_ABC, w.iters, label="125m-class fp32")
+
+
+def test_deterministic_and_batch_invariant(gpu):
+    import torch
+    shapes = [(768, 768), (768, 3072), (3072, 768), (300, 200)]
+    grads = [bf16_round(gaussian(s, 600 + i, 0.02))[1] for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 700 + i, 0.02) for i, s in enumerate(shapes)]
+    run = lambda g, m: run_muon(gpu, g, m, torch.bfloat16, torch.bfloat16, torch.bfloat16, BETA, MUON_ABC, 5, EPS)
+    m1, u1 = run(grads, moms)
+    m2, u2 = run(grads, moms)
+    for a, b in zip(u1, u2):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    for i in range(len(shapes)):
+        mi, ui = run([grads[i]], [moms[i]])
+        np.testing.assert_array_equal(ui[0].view(np.uint32), u1[i].view(np.uint32))
+        np.testing.assert_array_equal(mi[0].view(np.uint32), m1[i].view(np.uint32))
+
+
+def test_tall_is_transpose_of_wide(gpu):
+    import torch
+    g = gaussian((200, 520), 5)
+    m = gaussian((200, 520), 6)
+    _, uw = run_muon(gpu, [g], [m], torch.float32, torch.float32, torch.float32, BETA, MUON_ABC, 5, EPS)
+    _, ut = run_muon(gpu, [g.T.copy()], [m.T.copy()], torch.float32, torch.float32, torch.float32, BETA,
+                     MUON_ABC, 5, EPS)
+    assert rel_err(ut[0], uw[0].T) <= 1e-5
