@@ -1,0 +1,238 @@
+"""Benchmark of the owner-local Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b-class]
+
+One step = one muon_step_batched call over the whole owner set (momentum, Frobenius
+scaling, k Newton-Schulz iterations on every matrix), inputs resident in HBM.  The
+sign-vote workload's step is ns_orthogonalize over the 8 worker momenta followed by
+sign_pack per worker and one sign_vote.
+
+Prints ONE JSON line: matrix params/s (value), achieved TFLOP/s and % of the dense
+bf16 MFMA peak, a per-kernel breakdown from HIP events recorded by the library on the
+launch stream, the roofline of the dominant kernel and the fp64 CPU oracle timed on
+a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+NAMES = {"single-256x128": 1, "125m-class": 2, "1b-class-swiglu": 3, "7b-class": 4, "sign-vote-8x4096": 5}
+
+
+def ns_flops(shapes, iters):
+    """Algorithmic flops per kernel kind for one step: per matrix and iteration
+    m^2 n (upper triangle of X X^T), m^3 (A^2, symmetric), 2 m^2 n (B X)."""
+    syrk = poly = apply_ = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        syrk += m * m * n
+        poly += m ** 3
+        apply_ += 2 * m * m * n
+    return {"ns_syrk": syrk * iters, "ns_poly": poly * iters, "ns_apply": apply_ * iters}
+
+
+def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
+    """Algorithmic HBM bytes per step of the streaming kernels.
+    momentum_sumsq: read G and M, write M (or read x only); prep_operand: read M,
+    write X and X^T in the compute dtype."""
+    numel = sum(r * c for r, c in shapes)
+    mom = numel * (grad_bytes + 8) if momentum else numel * grad_bytes
+    src = 4 if momentum else grad_bytes
+    return {"momentum_sumsq": mom, "prep_operand": numel * (src + 2 * compute_bytes)}
+
+
+def cpu_baseline(wid, iters):
+    """The fp64 oracle on a bounded sample of the workload, on the host cores."""
+    import numpy as np
+    import oracle
+    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, host_matrix, MUON_ABC, BETA, EPS
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    w = WORKLOADS[wid]
+    shapes = w.shapes
+    # sample: the first matrix of each distinct shape, capped to ~10-30 s of CPU work
+    seen, sample = set(), []
+    for i, s in enumerate(shapes):
+        key = (min(s), max(s))
+        if key not in seen:
+            seen.add(key)
+            sample.append(i)
+    sample = sample[:2] if wid in (3, 4) else sample[:3]
+    params = 0
+    t0 = time.perf_counter()
+    for i in sample:
+        d = host_matrix(wid, i)
+        if wid == 5:
+            oracle.ns_orthogonalize(d["mom"], *MUON_ABC, iters, EPS)
+        else:
+            oracle.muon_step(d["grad"], d["mom"], BETA, *MUON_ABC, iters, EPS)
+        params += d["mom"].size
+    dt = time.perf_counter() - t0
+    desc = ", ".join(f"{shapes[i][0]}x{shapes[i][1]}" for i in sample)
+    return {"value": params / dt, "unit": "matrix params/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, {'NS' if wid == 5 else 'momentum + NS'}({iters}) on "
+                      f"matrices {desc} of the same workload, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="7b-class", choices=sorted(NAMES))
+    ap.add_argument("--compute", default=None, choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the owner-local step needs "
+              "no collective and this build measures the one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matrix_optimizers_sharded_amd as mo
+    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, device_matrix, MUON_ABC, BETA, EPS
+
+    wid = NAMES[args.workload]
+    w = WORKLOADS[wid]
+    dev = torch.device("cuda:0")
+    mo.load_library()
+    compute_name = args.compute or w.compute
+    compute = torch.bfloat16 if compute_name == "bf16" else torch.float32
+    shapes = w.shapes
+    print(f"[bench] workload {w.name}: {w.count} matrices, {w.numel / 1e9:.3f} G params, compute {compute_name}",
+          file=sys.stderr, flush=True)
+
+    ws = mo.Workspace(dev)
+    if wid == 5:
+        moms = [device_matrix(5, i, dev)[1] for i in range(w.count)]
+        outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+        nwords = (shapes[0][0] * shapes[0][1] + 31) // 32
+        packed = torch.empty((w.count, nwords), dtype=torch.int32, device=dev)
+        vote = torch.empty(nwords, dtype=torch.int32, device=dev)
+
+        def step():
+            mo.ns_orthogonalize(moms, outs, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
+            for i in range(w.count):
+                mo.sign_pack(outs[i], packed[i])
+            mo.sign_vote(packed, outs[0].numel(), out_packed=vote)
+    else:
+        grads, moms = [], []
+        for i in range(w.count):
+            g, m = device_matrix(wid, i, dev)
+            grads.append(g)
+            moms.append(m)
+        out_dtype = torch.bfloat16 if compute == torch.bfloat16 else torch.float32
+        outs = [torch.empty(s, dtype=out_dtype, device=dev) for s in shapes]
+
+        def step():
+            mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident, workspace {ws.buf.numel() / 2**30 if ws.buf is not None else 0:.1f} GiB "
+          f"after first call", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    mo.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = mo.profile_end()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    numel = w.numel
+    flops = ns_flops(shapes, w.iters)
+    f_alg = sum(flops.values())
+    tflops = f_alg / (ms / 1000.0) / 1e12
+    peak = PEAK_BF16_TFLOPS if compute == torch.bfloat16 else PEAK_F32_TFLOPS
+    es = 2 if compute == torch.bfloat16 else 4
+    gb = 2 if w.grad_dtype == "bf16" else 4
+    hbm = hbm_bytes(shapes, 4 if wid == 5 else gb, es, momentum=(wid != 5))
+
+    if wid == 5:
+        one = shapes[0][0] * shapes[0][1]
+        hbm["sign_pack"] = w.count * one * (es + 1 / 8)
+        hbm["sign_vote"] = one * (w.count + 1) / 8
+
+    def per_launch(name):
+        launches, total = kernels[name]
+        lps = launches / args.steps
+        work = flops.get(name, hbm.get(name, 0.0)) / lps
+        return lps, total / launches, work
+
+    breakdown = {}
+    for name in kernels:
+        lps, pl_ms, work = per_launch(name)
+        entry = {"launches_per_step": lps, "ms_per_launch": round(pl_ms, 4),
+                 "ms_per_step": round(pl_ms * lps, 4)}
+        if name in flops:
+            entry["tflops"] = round(work / (pl_ms / 1e3) / 1e12, 2)
+        elif name in hbm:
+            entry["gbs"] = round(work / (pl_ms / 1e3) / 1e9, 1)
+        breakdown[name] = entry
+    dom = max(kernels.items(), key=lambda kv: kv[1][1])[0] if kernels else None
+    roofline = None
+    if dom in flops:
+        _, pl_ms, work = per_launch(dom)
+        achieved = work / (pl_ms / 1e3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    elif dom in hbm:
+        _, pl_ms, work = per_launch(dom)
+        achieved = work / (pl_ms / 1e3) / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wid, w.iters)
+
+    line = {
+        "metric": "NS-orthogonalized params/sec + MFMA TFLOP/s (% peak), 7B layer shapes",
+        "value": numel / (ms / 1000.0),
+        "unit": "matrix params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": compute_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "matrices": w.count, "params": numel, "ns_iters": w.iters,
+                   "grad_dtype": w.grad_dtype, "momentum_dtype": "f32", "accumulate": "f32",
+                   "coefficients": list(MUON_ABC), "beta": BETA, "parallelism": "single GPU (owner-local)"},
+        "tflops": round(tflops, 2),
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "flops_per_step": f_alg,
+        "kernels": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
