@@ -141,13 +141,13 @@ def main():
         def step():
             mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
     torch.cuda.synchronize()
-    print(f"[bench] inputs resident, workspace {ws.buf.numel() / 2**30 if ws.buf is not None else 0:.1f} GiB "
-          f"after first call", file=sys.stderr, flush=True)
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
-        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+        print(f"[bench] warmup {i + 1}/{args.warmup} done (workspace {ws.buf.numel() / 2**30:.1f} GiB)",
+              file=sys.stderr, flush=True)
 
     mo.profile_begin()
     torch.cuda.synchronize()

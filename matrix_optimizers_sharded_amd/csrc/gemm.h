@@ -14,10 +14,13 @@
 // bounds checks; only the final write to the caller's buffer is clipped.
 //
 // Tiling (gfx950, wave64): 256x256 block tile, 4 waves in 2x2, each wave owns a
-// 128x128 sub-tile = 4x4 MFMA 32x32 blocks (256 fp32 accumulators per lane).  The
-// k-loop stages 128-byte rows (64 bf16 or 32 fp32) of both operands through LDS,
-// double-buffered through registers, with rows padded to 144 bytes so the 16-byte
-// fragment reads of 8 or 16 consecutive rows fall in distinct banks.
+// 128x128 sub-tile = 4x4 MFMA 32x32 blocks (256 fp32 accumulators per lane, held in
+// AGPRs).  The k-loop streams 128-byte row slabs (64 bf16 or 32 fp32 of k) of both
+// operands straight from HBM/L2 into LDS with 16-byte buffer loads that write LDS
+// directly (no register staging), through a 2-stage ring: the loads of slab t+1
+// are in flight while slab t is multiplied.  LDS rows are 128 bytes with the 16-byte
+// chunk index XOR-swizzled by (r ^ r>>1) & 7, so the fragment reads of 8 or 16
+// consecutive rows hit distinct banks.
 #pragma once
 
 #include "common.h"
@@ -28,9 +31,16 @@ enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3 };
 
 constexpr int GT = GEMM_TILE;          // 256
 constexpr int ROW_BYTES = 128;         // one k-slab row of an operand tile
-constexpr int LDS_ROW = 144;           // padded LDS row pitch
-constexpr int OPERAND_BYTES = GT * LDS_ROW;            // 36864
-constexpr int GEMM_LDS_BYTES = 4 * OPERAND_BYTES;      // 2 stages x {P, Q} = 147456
+constexpr int OPERAND_BYTES = GT * ROW_BYTES;          // 32768
+constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;         // P and Q
+constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES;        // 2 stages = 131072
+
+// raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
+constexpr int RSRC_FLAGS = 0x00020000;
+
+__device__ inline int swz(int r) { return (r ^ (r >> 1)) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <typename T> struct Mfma;
 
@@ -76,7 +86,7 @@ template <> __device__ inline void store4<float>(float* p, float v0, float v1, f
 template <typename T, int MODE, typename TO>
 __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
                                                     int parity, float ca, float cb, float cc) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[GEMM_LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
   const int64_t item = blockIdx.x;
   const MatDesc& d = descs[find_desc(descs, count, kind, item)];
@@ -113,14 +123,35 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
 
-  // global -> register staging: thread loads 16-byte chunk (tid & 7) of rows
-  // (tid >> 3) + 32 q, q = 0..7, of each operand's 256 x 128-byte slab
-  constexpr int KE = ROW_BYTES / sizeof(T);   // k elements per slab
-  const int lrow = tid >> 3, lch = tid & 7;
-  const unsigned char* gp = reinterpret_cast<const unsigned char*>(P + (i0 + lrow) * ldp) + lch * 16;
-  const unsigned char* gq = reinterpret_cast<const unsigned char*>(Q + (j0 + lrow) * ldq) + lch * 16;
-  const int64_t stp = 32 * ldp * sizeof(T), stq = 32 * ldq * sizeof(T);
-  uint4 rp[8], rq[8];
+  // Direct-to-LDS loads: wave w, instruction q fills rows 8*(4q+w) .. +7 of an
+  // operand slab (1 KiB contiguous in LDS: lane l -> row 8*(4q+w) + l/8, physical
+  // chunk l%8).  The lane fetches the logical chunk that the swizzle stores there.
+  const uint32_t esz = sizeof(T);
+  const uint32_t rowsP = d.mp;   // X, A and B all have mp rows
+  const uint32_t rowsQ = (MODE == GM_APPLY || MODE == GM_APPLY_FINAL) ? d.np : d.mp;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(P), 0, static_cast<int>(rowsP * static_cast<uint32_t>(ldp) * esz), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(Q), 0, static_cast<int>(rowsQ * static_cast<uint32_t>(ldq) * esz), RSRC_FLAGS);
+  uint32_t vP[8], vQ[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = 8 * (4 * q + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    vP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
+    vQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
+  }
+  auto issue = [&](int kt, int stage) {
+    const int soff = kt * ROW_BYTES;
+    unsigned char* base = smem + stage * STAGE_BYTES + wave * 1024;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * 4096), 16, vP[q], soff, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * 4096), 16, vQ[q],
+                                               soff, 0, 0);
+  };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -130,59 +161,48 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int nk = K / KE;
-  // prologue: slab 0
+  // fragment read offsets (row part), per sub-block
+  int rowA[4], rowB[4];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    rp[q] = *reinterpret_cast<const uint4*>(gp + q * stp);
-    rq[q] = *reinterpret_cast<const uint4*>(gq + q * stq);
+  for (int a = 0; a < 4; ++a) {
+    rowA[a] = wm + a * 32 + l32;
+    rowB[a] = wn + a * 32 + l32;
   }
-  {
-    unsigned char* sp = smem + lrow * LDS_ROW + lch * 16;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      *reinterpret_cast<uint4*>(sp + q * 32 * LDS_ROW) = rp[q];
-      *reinterpret_cast<uint4*>(sp + OPERAND_BYTES + q * 32 * LDS_ROW) = rq[q];
-    }
-  }
-  __syncthreads();
 
+  typedef typename Mfma<T>::frag frag_t;
+  const int KE = ROW_BYTES / sizeof(T);
+  const int nk = K / KE;
+  issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const int64_t off = static_cast<int64_t>(kt + 1) * ROW_BYTES;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        rp[q] = *reinterpret_cast<const uint4*>(gp + off + q * stp);
-        rq[q] = *reinterpret_cast<const uint4*>(gq + off + q * stq);
-      }
-    }
-    const unsigned char* sP = smem + cur * 2 * OPERAND_BYTES;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    const unsigned char* sP = smem + (kt & 1) * STAGE_BYTES;
     const unsigned char* sQ = sP + OPERAND_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      typename Mfma<T>::frag fa[4], fb[4];
-      const int cofs = (2 * kk + half) * 16;
+    // fragments double-buffered across the four k16 steps of the slab: the reads of
+    // step kk+1 are issued between the MFMAs of step kk
+    frag_t fa[2][4], fb[2][4];
+    auto read_frags = [&](int kk, frag_t* A, frag_t* B) {
+      const int c = 2 * kk + half;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        fa[a] = *reinterpret_cast<const typename Mfma<T>::frag*>(sP + (wm + a * 32 + l32) * LDS_ROW + cofs);
+        A[a] = *reinterpret_cast<const frag_t*>(sP + rowA[a] * ROW_BYTES + ((c ^ swz(rowA[a])) << 4));
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        fb[b] = *reinterpret_cast<const typename Mfma<T>::frag*>(sQ + (wn + b * 32 + l32) * LDS_ROW + cofs);
+        B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
+    };
+    read_frags(0, fa[0], fb[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      if (kk < 3) read_frags(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], fa[a], fb[b]);
+        for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], fa[cur][a], fb[cur][b]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) {
-      unsigned char* sp = smem + (cur ^ 1) * 2 * OPERAND_BYTES + lrow * LDS_ROW + lch * 16;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        *reinterpret_cast<uint4*>(sp + q * 32 * LDS_ROW) = rp[q];
-        *reinterpret_cast<uint4*>(sp + OPERAND_BYTES + q * 32 * LDS_ROW) = rq[q];
-      }
-    }
-    __syncthreads();
   }
 
   // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds

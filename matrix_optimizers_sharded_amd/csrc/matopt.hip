@@ -106,6 +106,10 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.vec_ok = (aligned16(d.grad) && aligned16(d.mom) && aligned16(d.out) && (mt.cols % 4 == 0)) ? 1 : 0;
     d.scale_slot = k;
     const size_t xb = size_t(d.mp) * size_t(d.np) * es, ab = size_t(d.mp) * size_t(d.mp) * es;
+    // the GEMM addresses each operand buffer with 32-bit byte offsets
+    if (xb > size_t(0x7fffffff))
+      return fail(MO_ERR_UNSUPPORTED, "matrix " + std::to_string(order[k]) +
+                                          ": padded operand exceeds 2 GiB (min(rows,cols) * max(rows,cols))");
     auto take = [&](size_t nb) {
       void* p = base ? static_cast<void*>(base + off) : nullptr;
       off = align_up(off + nb, ALIGN);

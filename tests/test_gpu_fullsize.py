@@ -1,0 +1,134 @@
+"""Full-size parity: whole owner sets in one batched call, exactly as the benchmark
+launches them, checked against the fp64 oracle on sampled matrices (the oracle runs
+one matrix at a time) and by properties that hold for every matrix.
+
+Sampled matrices come from the host generator (so the oracle sees the same values);
+the rest of the owner set comes from the device generator with the same
+distributions.  A matrix's result does not depend on the rest of the batch (checked
+bit-exactly in test_gpu_parity.py), so this is the same computation the benchmark
+times."""
+
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from matrix_optimizers_sharded_amd.workloads import (
+    MUON_ABC, BETA, EPS, WORKLOADS, host_matrix, device_matrix, f32_to_bf16_bits)
+from gpu_util import say, to_dev_f32, to_dev_bf16, host_f32, rel_err
+from pins import scalar_poly_iterate
+
+pytestmark = pytest.mark.gpu
+
+
+def band_top(abc, iters):
+    s = np.linspace(0.0, 1.0, 200001)
+    return float(np.max(scalar_poly_iterate(s, *abc, iters)))
+
+
+def spectral_norm(t, iters=30):
+    """Power iteration on U^T U in fp32 (device), a lower bound that converges to
+    sigma_max."""
+    import torch
+    x = t.float()
+    v = torch.ones(x.shape[1], device=x.device) / x.shape[1] ** 0.5
+    s = torch.zeros((), device=x.device)
+    for _ in range(iters):
+        w = x.t() @ (x @ v)
+        s = w.norm()
+        v = w / s
+    return float(s.sqrt())
+
+
+def run_owner_set(gpu, wid, sample):
+    import torch
+    from matrix_optimizers_sharded_amd import muon_step_batched
+    w = WORKLOADS[wid]
+    grads, moms, host = [], [], {}
+    for i in range(w.count):
+        if i in sample:
+            d = host_matrix(wid, i)
+            host[i] = d
+            grads.append(to_dev_bf16(d["grad_bits"], gpu))
+            moms.append(to_dev_f32(d["mom"], gpu))
+        else:
+            g, m = device_matrix(wid, i, gpu)
+            grads.append(g)
+            moms.append(m)
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=gpu) for s in w.shapes]
+    say(f"{w.name}: {w.count} matrices resident, running one batched step")
+    muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=torch.bfloat16)
+    torch.cuda.synchronize()
+    return w, grads, moms, outs, host
+
+
+def check_owner_set(wid, sample, gpu):
+    import torch
+    w, grads, moms, outs, host = run_owner_set(gpu, wid, sample)
+    top = band_top(MUON_ABC, w.iters)
+    for i, u in enumerate(outs):
+        assert bool(torch.isfinite(u.float()).all()), f"matrix {i} not finite"
+    for i in range(0, w.count, max(1, w.count // 16)):
+        s = spectral_norm(outs[i])
+        assert s <= top * 1.02 + 1e-3, f"matrix {i}: sigma_max {s:.4f} above the band top {top:.4f}"
+    for i in sample:
+        d = host[i]
+        say(f"{w.name}: oracle on matrix {i} {d['shape']}")
+        want_m, want_u = oracle.muon_step(d["grad"], d["mom"], BETA, *MUON_ABC, w.iters, EPS)
+        np.testing.assert_array_equal(host_f32(moms[i]).view(np.uint32), want_m.view(np.uint32))
+        e = rel_err(host_f32(outs[i]), want_u)
+        say(f"{w.name}: matrix {i} rel err {e:.3e}")
+        assert e <= 2e-2, (i, e)
+    del grads, moms, outs
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_1b_class_swiglu_heavy_tailed(gpu):
+    # one of each shape (2048^2, 2048x5632, 5632x2048) from the first and last layer
+    check_owner_set(3, [0, 4, 6, 105, 111], gpu)
+
+
+@pytest.mark.timeout(1200)
+def test_7b_class_owner_set(gpu):
+    # 4096^2, 4096x11008, 11008x4096 from layer 0, and the last matrix of layer 31
+    check_owner_set(4, [0, 4, 6, 223], gpu)
+
+
+@pytest.mark.timeout(900)
+def test_sign_muon_vote_8x4096(gpu):
+    import torch
+    from matrix_optimizers_sharded_amd import ns_orthogonalize, sign_pack, sign_vote
+    w = WORKLOADS[5]
+    ins = [host_matrix(5, i)["mom"] for i in range(w.count)]
+    xs = [to_dev_f32(m, gpu) for m in ins]
+    outs = [torch.empty(m.shape, dtype=torch.bfloat16, device=gpu) for m in ins]
+    say("sign-vote-8x4096: NS(5) on 8 worker momenta")
+    ns_orthogonalize(xs, outs, *MUON_ABC, w.iters, EPS, compute=torch.bfloat16)
+    numel = ins[0].size
+    nwords = (numel + 31) // 32
+    packed = torch.empty((w.count, nwords), dtype=torch.int32, device=gpu)
+    for i in range(w.count):
+        sign_pack(outs[i], packed[i])
+    vote, sums = sign_vote(packed, numel, with_sums=True)
+    torch.cuda.synchronize()
+    u_gpu = [host_f32(o) for o in outs]
+    p_gpu = packed.cpu().numpy().view(np.uint32)
+    # integer stages: bit-exact on the GPU's own float U
+    for i in range(w.count):
+        np.testing.assert_array_equal(p_gpu[i], oracle.sign_pack(u_gpu[i]))
+    want_v, want_s = oracle.majority_vote(p_gpu, numel)
+    np.testing.assert_array_equal(vote.cpu().numpy().view(np.uint32), want_v)
+    np.testing.assert_array_equal(sums.cpu().numpy().astype(np.int64), want_s)
+    # float stage on two sampled workers, and where the signs may differ
+    for i in (0, 7):
+        say(f"sign-vote-8x4096: oracle NS on worker {i}")
+        u_or = oracle.ns_orthogonalize(ins[i], *MUON_ABC, w.iters, EPS)
+        e = rel_err(u_gpu[i], u_or)
+        assert e <= 2e-2, (i, e)
+        flips = (u_gpu[i] >= 0) != (u_or >= 0)
+        scale = 8.0 * np.linalg.norm(u_gpu[i] - u_or) / np.sqrt(numel)
+        say(f"worker {i}: rel err {e:.3e}, sign flips {flips.mean():.2e}")
+        assert np.all(np.abs(u_or[flips]) <= scale), "a sign flipped where the oracle value is large"
