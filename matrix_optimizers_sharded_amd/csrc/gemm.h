@@ -42,6 +42,9 @@ __device__ inline int swz(int r) { return (r ^ (r >> 1)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 0
+constexpr int WAIT_VM0_LGKM0 = 0x0070;
+
 template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16_t> {
@@ -63,14 +66,63 @@ template <> struct Mfma<float> {
   }
 };
 
-// local upper-triangle index -> (ti, tj), ti <= tj, row-major over the triangle
-__device__ inline void upper_tile(int64_t local, int T, int& ti, int& tj) {
-  int r = 0;
-  int64_t L = local;
-  while (L >= T - r) { L -= T - r; ++r; }
-  ti = r;
-  tj = r + static_cast<int>(L);
+// Tile order inside one matrix: rows of tiles are cut into bands of BAND rows; a
+// band is walked column by column, top to bottom within a column.  Consecutive
+// items (which run at the same time on one XCD) then form a BAND x 8 block whose
+// operand row-panels are shared through that XCD's L2.
+#ifndef MO_GEMM_BAND
+#define MO_GEMM_BAND 1
+#endif
+#ifndef MO_GEMM_XCD_REMAP
+#define MO_GEMM_XCD_REMAP 0
+#endif
+constexpr int BAND = MO_GEMM_BAND;
+
+__device__ inline void rect_tile(int64_t local, int tm, int tn, int& ti, int& tj) {
+  const int64_t per_band = static_cast<int64_t>(BAND) * tn;
+  const int b = static_cast<int>(local / per_band);
+  const int r = static_cast<int>(local - b * per_band);
+  const int h = min(BAND, tm - b * BAND);
+  tj = r / h;
+  ti = b * BAND + r % h;
 }
+
+// Upper triangle (ti <= tj) of a T x T tile grid in the same banded order.
+__device__ inline void upper_tile(int64_t local, int T, int& ti, int& tj) {
+  int b = 0;
+  for (;; ++b) {
+    const int h = min(BAND, T - b * BAND);
+    const int64_t n = static_cast<int64_t>(h) * (h + 1) / 2 + static_cast<int64_t>(T - b * BAND - h) * h;
+    if (local < n) break;
+    local -= n;
+  }
+  const int r0 = b * BAND, h = min(BAND, T - r0);
+  // first h columns of the band hold 1, 2, ..., h tiles; the rest hold h
+  int c = 0;
+  for (; c < h; ++c) {
+    if (local < c + 1) break;
+    local -= c + 1;
+  }
+  if (c < h) {
+    ti = r0 + static_cast<int>(local);
+    tj = r0 + c;
+  } else {
+    tj = r0 + h + static_cast<int>(local / h);
+    ti = r0 + static_cast<int>(local % h);
+  }
+}
+
+// Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  Give XCD x the
+// contiguous slice x of the work list so that its concurrent blocks are neighbours.
+__device__ inline int64_t xcd_remap(int64_t b, int64_t total) {
+  const int64_t per = total / 8, rem = total % 8;
+  const int64_t x = b % 8, k = b / 8;
+  return x * per + min(x, rem) + k;
+}
+
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16_t> { typedef bf16x4_t type; };
+template <> struct Vec4<float> { typedef f32x4_t type; };
 
 template <typename T>
 __device__ inline void store4(T* p, float v0, float v1, float v2, float v3);
@@ -88,7 +140,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
                                                     int parity, float ca, float cb, float cc) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
-  const int64_t item = blockIdx.x;
+  const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
   const MatDesc& d = descs[find_desc(descs, count, kind, item)];
   const int64_t local = item - d.begin[kind];
 
@@ -108,9 +160,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     ldp = ldq = d.mp;
     K = d.mp;
   } else {
-    const int tn = d.np / GT;
-    ti = static_cast<int>(local / tn);
-    tj = static_cast<int>(local % tn);
+    rect_tile(local, d.mp / GT, d.np / GT, ti, tj);
     P = static_cast<const T*>(d.B);
     Q = static_cast<const T*>(d.XT[parity]);
     ldp = ldq = d.mp;
@@ -172,48 +222,79 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   typedef typename Mfma<T>::frag frag_t;
   const int KE = ROW_BYTES / sizeof(T);
   const int nk = K / KE;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    const unsigned char* sP = smem + (kt & 1) * STAGE_BYTES;
+  // Pipeline per slab kt (stage kt&1), fragments double-buffered over k16 steps:
+  //   steps 0..2: read the next step's fragments, 16 MFMAs on the current ones;
+  //   then wait for this wave's loads of slab kt+1 and for its last LDS reads, one
+  //   barrier (slab kt+1 is in LDS for everyone; stage kt&1 is free), start the
+  //   loads of slab kt+2 into stage kt&1, read slab kt+1's first fragments;
+  //   step 3: 16 MFMAs, which hide that barrier and those reads.
+  frag_t fa[2][4], fb[2][4];
+  auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
-    // fragments double-buffered across the four k16 steps of the slab: the reads of
-    // step kk+1 are issued between the MFMAs of step kk
-    frag_t fa[2][4], fb[2][4];
-    auto read_frags = [&](int kk, frag_t* A, frag_t* B) {
-      const int c = 2 * kk + half;
+    const int c = 2 * kk + half;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        A[a] = *reinterpret_cast<const frag_t*>(sP + rowA[a] * ROW_BYTES + ((c ^ swz(rowA[a])) << 4));
+    for (int a = 0; a < 4; ++a)
+      A[a] = *reinterpret_cast<const frag_t*>(sP + rowA[a] * ROW_BYTES + ((c ^ swz(rowA[a])) << 4));
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
-    };
-    read_frags(0, fa[0], fb[0]);
+    for (int b = 0; b < 4; ++b)
+      B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
+  };
+  auto mfma_step = [&](const frag_t* A, const frag_t* B) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1;
-      if (kk < 3) read_frags(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
+  };
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+  __syncthreads();
+  if (nk > 1) issue(1, 1);
+  read_frags(smem, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char* sP = smem + (kt & 1) * STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      read_frags(sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], fa[cur][a], fb[cur][b]);
+      mfma_step(fa[kk & 1], fb[kk & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+      __syncthreads();
+      if (kt + 2 < nk) issue(kt + 2, kt & 1);
+      read_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, fa[0], fb[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
+  // ib..ib+3 of one column j per register group g.  Values the epilogue needs at
+  // [ib..ib+3][j] are read as one vector from a transposed copy: A[j][ib..] (A is
+  // symmetric) for POLY and X^T[j][ib..] for APPLY.  Loads are issued a whole
+  // sub-block row (16 vectors) at a time before any of them is used.
+  typedef typename Vec4<T>::type v4_t;
+  const int64_t ldt = d.mp;
   if (MODE == GM_SYRK || MODE == GM_POLY) {
     T* C = static_cast<T*>(MODE == GM_SYRK ? d.A : d.B);
     const T* Ain = static_cast<const T*>(d.A);
-    const int64_t ld = d.mp;
     const bool diag = (ti == tj);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a) {
+      v4_t e[4][4];
+      if (MODE == GM_POLY) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+            const int j = j0 + wn + b * 32 + l32;
+            e[b][g] = *reinterpret_cast<const v4_t*>(Ain + static_cast<int64_t>(j) * ldt + ib);
+          }
+      }
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -224,32 +305,43 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             v[t] = acc[a][b][4 * g + t];
-            if (MODE == GM_POLY) v[t] = cb * to_f32(Ain[(ib + t) * ld + j]) + cc * v[t];
+            if (MODE == GM_POLY) v[t] = cb * to_f32(e[b][g][t]) + cc * v[t];
           }
           if (!diag) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) C[(ib + t) * ld + j] = from_f32<T>(v[t]);
-            store4<T>(C + static_cast<int64_t>(j) * ld + ib, v[0], v[1], v[2], v[3]);
+            for (int t = 0; t < 4; ++t) C[static_cast<int64_t>(ib + t) * ldt + j] = from_f32<T>(v[t]);
+            store4<T>(C + static_cast<int64_t>(j) * ldt + ib, v[0], v[1], v[2], v[3]);
           } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i = ib + t;
               if (i <= j) {
                 const T x = from_f32<T>(v[t]);
-                C[static_cast<int64_t>(i) * ld + j] = x;
-                C[static_cast<int64_t>(j) * ld + i] = x;
+                C[static_cast<int64_t>(i) * ldt + j] = x;
+                C[static_cast<int64_t>(j) * ldt + i] = x;
               }
             }
           }
         }
+    }
   } else {
     T* X = static_cast<T*>(d.X);
+    const T* XTc = static_cast<const T*>(d.XT[parity]);
     T* XTn = static_cast<T*>(d.XT[parity ^ 1]);
-    const int64_t ldx = d.np, ldt = d.mp;
+    const int64_t ldx = d.np;
     TO* out = static_cast<TO*>(d.out);
     const int m = d.m, n = d.n;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a) {
+      v4_t e[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+          const int j = j0 + wn + b * 32 + l32;
+          e[b][g] = *reinterpret_cast<const v4_t*>(XTc + static_cast<int64_t>(j) * ldt + ib);
+        }
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -258,8 +350,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
           const int j = j0 + wn + b * 32 + l32;
           float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            v[t] = ca * to_f32(X[static_cast<int64_t>(ib + t) * ldx + j]) + acc[a][b][4 * g + t];
+          for (int t = 0; t < 4; ++t) v[t] = ca * to_f32(e[b][g][t]) + acc[a][b][4 * g + t];
           if (MODE == GM_APPLY) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) X[static_cast<int64_t>(ib + t) * ldx + j] = from_f32<T>(v[t]);
@@ -283,6 +374,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
             }
           }
         }
+    }
   }
 }
 
