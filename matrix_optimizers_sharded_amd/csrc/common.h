@@ -26,6 +26,9 @@ enum Kind {
 constexpr int GEMM_TILE = 256;   // workspace dims are padded to multiples of this
 constexpr int PREP_TILE = 64;
 constexpr int CHUNK = 4096;      // elements per momentum / sum-of-squares block
+// Workspace rows are padded by 128 bytes so that no buffer has a power-of-two row
+// pitch: rows read together by one load instruction then spread over L2 channels.
+constexpr int LD_PAD_BYTES = 128;
 
 struct MatDesc {
   // caller buffers
@@ -35,6 +38,7 @@ struct MatDesc {
   int64_t rows, cols, numel;
   // oriented problem: X is m x n with m = min(rows, cols), n = max(rows, cols)
   int32_t m, n, mp, np;   // mp, np: m and n rounded up to GEMM_TILE
+  int32_t ldx, ldm;       // row pitch (elements) of X (>= np) and of X^T, A, B (>= mp)
   int32_t transposed;     // 1 if rows > cols (X = M^T)
   int32_t vec_ok;         // 1 if grad/mom/out allow 16-byte vector access
   // workspace buffers, compute dtype, zero outside the m x n corner
@@ -45,7 +49,7 @@ struct MatDesc {
   int64_t begin[NKIND];   // first work item of this matrix per launch kind
   int64_t items[NKIND];   // work items of this matrix per launch kind
   int32_t scale_slot;     // index into the per-matrix scale array
-  int32_t pad_;
+  int32_t pad_[3];
 };
 
 __device__ inline int find_desc(const MatDesc* __restrict__ d, int count, int kind, int64_t item) {

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
   __syncthreads();
   TC* X = static_cast<TC*>(d.X);
   TC* XT = static_cast<TC*>(d.XT[0]);
-  const int64_t ldx = d.np, ldt = d.mp;
+  const int64_t ldx = d.ldx, ldt = d.ldm;
 #pragma unroll 4
   for (int q = 0; q < 16; ++q) {
     const int a = ty + 4 * q;

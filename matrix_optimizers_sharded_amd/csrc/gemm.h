@@ -30,20 +30,53 @@ namespace mo {
 enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3 };
 
 constexpr int GT = GEMM_TILE;          // 256
-constexpr int ROW_BYTES = 128;         // one k-slab row of an operand tile
-constexpr int OPERAND_BYTES = GT * ROW_BYTES;          // 32768
+
+// k-slab geometry: each operand row of a slab is ROW_BYTES (64: 32 bf16 / 16 fp32 of
+// k), and NSTAGE slabs are in flight in an LDS ring, so the loads of slab t+NSTAGE-1
+// overlap the MFMAs of slabs t .. t+NSTAGE-2.
+#ifndef MO_GEMM_SLAB_BYTES
+#define MO_GEMM_SLAB_BYTES 128
+#endif
+#ifndef MO_GEMM_STAGES
+#define MO_GEMM_STAGES 2
+#endif
+// operand path into LDS: 0 = direct-to-LDS buffer loads, 1 = buffer loads into
+// registers one slab ahead, then ds_write_b128 (2 LDS stages)
+#ifndef MO_GEMM_LOAD_PATH
+#define MO_GEMM_LOAD_PATH 0
+#endif
+constexpr int ROW_BYTES = MO_GEMM_SLAB_BYTES;
+constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
+constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
+constexpr int NSTAGE = MO_GEMM_STAGES;
+constexpr int OPERAND_BYTES = GT * ROW_BYTES;
 constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;         // P and Q
-constexpr int GEMM_LDS_BYTES = 2 * STAGE_BYTES;        // 2 stages = 131072
+constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
+constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;        // rows one 1 KiB wave load fills
+constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / 4;  // per wave, per slab
+constexpr int INST_PER_SLAB = 2 * INST_PER_OPERAND;
+static_assert(GEMM_LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
+static_assert(MO_GEMM_LOAD_PATH == 0 || NSTAGE == 2, "the register path uses two LDS stages");
+constexpr int NPASS = OPERAND_BYTES / (256 * 16);      // 16-byte loads per thread, per operand
+static_assert(NSTAGE * (ROW_BYTES / 2) <= 256, "the ring must not be deeper than the shortest K (256)");
+static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
 
 // raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
 constexpr int RSRC_FLAGS = 0x00020000;
 
-__device__ inline int swz(int r) { return (r ^ (r >> 1)) & 7; }
+// 16-byte chunk swizzle inside a row, chosen so that the fragment reads of 8
+// consecutive rows (32 banks x 4 B) and of 16 consecutive rows (64 banks) fall in
+// distinct banks.
+__device__ inline int swz(int r) {
+  if (CHUNKS == 8) return (r ^ (r >> 1)) & 7;
+  return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 0
-constexpr int WAIT_VM0_LGKM0 = 0x0070;
+// s_waitcnt immediate (gfx9 encoding): vmcnt = N (bits 3:0 and 15:14), expcnt = 7
+// (no wait), lgkmcnt = 0
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 template <typename T> struct Mfma;
 
@@ -71,10 +104,10 @@ template <> struct Mfma<float> {
 // items (which run at the same time on one XCD) then form a BAND x 8 block whose
 // operand row-panels are shared through that XCD's L2.
 #ifndef MO_GEMM_BAND
-#define MO_GEMM_BAND 1
+#define MO_GEMM_BAND 4
 #endif
 #ifndef MO_GEMM_XCD_REMAP
-#define MO_GEMM_XCD_REMAP 0
+#define MO_GEMM_XCD_REMAP 1
 #endif
 constexpr int BAND = MO_GEMM_BAND;
 
@@ -112,12 +145,20 @@ __device__ inline void upper_tile(int64_t local, int T, int& ti, int& tj) {
   }
 }
 
-// Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  Give XCD x the
-// contiguous slice x of the work list so that its concurrent blocks are neighbours.
+// Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  Remap so that
+// XCD x receives runs of XCD_CHUNK consecutive work items (chunks dealt round-robin
+// over the XCDs): the blocks one XCD runs at a time are neighbours in the work
+// list and share operand panels in that XCD's L2, while all XCDs still progress
+// through the list together (equal load).
+#ifndef MO_GEMM_XCD_CHUNK
+#define MO_GEMM_XCD_CHUNK 32
+#endif
 __device__ inline int64_t xcd_remap(int64_t b, int64_t total) {
-  const int64_t per = total / 8, rem = total % 8;
-  const int64_t x = b % 8, k = b / 8;
-  return x * per + min(x, rem) + k;
+  constexpr int64_t G = MO_GEMM_XCD_CHUNK;
+  const int64_t full = total / (8 * G) * (8 * G);   // blocks in complete rounds
+  if (b >= full) return b;                          // ragged tail: identity
+  const int64_t x = b % 8, k = b / 8;               // k-th block of XCD x
+  return (k / G) * (8 * G) + x * G + (k % G);
 }
 
 template <typename T> struct Vec4;
@@ -152,18 +193,18 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   if (MODE == GM_SYRK) {
     upper_tile(local, d.mp / GT, ti, tj);
     P = Q = static_cast<const T*>(d.X);
-    ldp = ldq = d.np;
+    ldp = ldq = d.ldx;
     K = d.np;
   } else if (MODE == GM_POLY) {
     upper_tile(local, d.mp / GT, ti, tj);
     P = Q = static_cast<const T*>(d.A);
-    ldp = ldq = d.mp;
+    ldp = ldq = d.ldm;
     K = d.mp;
   } else {
     rect_tile(local, d.mp / GT, d.np / GT, ti, tj);
     P = static_cast<const T*>(d.B);
     Q = static_cast<const T*>(d.XT[parity]);
-    ldp = ldq = d.mp;
+    ldp = ldq = d.ldm;
     K = d.mp;
   }
   const int i0 = ti * GT, j0 = tj * GT;
@@ -173,9 +214,10 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
 
-  // Direct-to-LDS loads: wave w, instruction q fills rows 8*(4q+w) .. +7 of an
-  // operand slab (1 KiB contiguous in LDS: lane l -> row 8*(4q+w) + l/8, physical
-  // chunk l%8).  The lane fetches the logical chunk that the swizzle stores there.
+  // Direct-to-LDS loads: wave w, instruction q fills ROWS_PER_INST rows starting at
+  // ROWS_PER_INST*(4q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
+  // row + l/CHUNKS, physical chunk l%CHUNKS); the lane fetches the logical chunk
+  // that the swizzle stores there.
   const uint32_t esz = sizeof(T);
   const uint32_t rowsP = d.mp;   // X, A and B all have mp rows
   const uint32_t rowsQ = (MODE == GM_APPLY || MODE == GM_APPLY_FINAL) ? d.np : d.mp;
@@ -183,11 +225,11 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
       const_cast<T*>(P), 0, static_cast<int>(rowsP * static_cast<uint32_t>(ldp) * esz), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(Q), 0, static_cast<int>(rowsQ * static_cast<uint32_t>(ldq) * esz), RSRC_FLAGS);
-  uint32_t vP[8], vQ[8];
+  uint32_t vP[INST_PER_OPERAND], vQ[INST_PER_OPERAND];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = 8 * (4 * q + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(row);
+  for (int q = 0; q < INST_PER_OPERAND; ++q) {
+    const int row = ROWS_PER_INST * (4 * q + wave) + lane / CHUNKS;
+    const int c = (lane % CHUNKS) ^ swz(row);
     vP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
     vQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
   }
@@ -195,12 +237,41 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     const int soff = kt * ROW_BYTES;
     unsigned char* base = smem + stage * STAGE_BYTES + wave * 1024;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < INST_PER_OPERAND; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * 4096), 16, vP[q], soff, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < INST_PER_OPERAND; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * 4096), 16, vQ[q],
                                                soff, 0, 0);
+  };
+
+  // Register path: thread t moves logical chunk t % CHUNKS of rows
+  // (256 / CHUNKS) * q + t / CHUNKS; the LDS position applies the same swizzle.
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  uint32_t gP[NPASS], gQ[NPASS], lOff[NPASS];
+#pragma unroll
+  for (int q = 0; q < NPASS; ++q) {
+    const int row = (256 / CHUNKS) * q + tid / CHUNKS;
+    const int c = tid % CHUNKS;
+    gP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
+    gQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
+    lOff[q] = row * ROW_BYTES + ((c ^ swz(row)) << 4);
+  }
+  u32x4_t rgP[MO_GEMM_LOAD_PATH ? NPASS : 1], rgQ[MO_GEMM_LOAD_PATH ? NPASS : 1];
+  auto load_regs = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < (MO_GEMM_LOAD_PATH ? NPASS : 0); ++q) {
+      rgP[q] = __builtin_amdgcn_raw_buffer_load_b128(rP, gP[q], kt * ROW_BYTES, 0);
+      rgQ[q] = __builtin_amdgcn_raw_buffer_load_b128(rQ, gQ[q], kt * ROW_BYTES, 0);
+    }
+  };
+  auto write_lds = [&](int stage) {
+    unsigned char* base = smem + stage * STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < (MO_GEMM_LOAD_PATH ? NPASS : 0); ++q) {
+      *reinterpret_cast<u32x4_t*>(base + lOff[q]) = rgP[q];
+      *reinterpret_cast<u32x4_t*>(base + OPERAND_BYTES + lOff[q]) = rgQ[q];
+    }
   };
 
   f32x16_t acc[4][4];
@@ -221,13 +292,15 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
 
   typedef typename Mfma<T>::frag frag_t;
   const int KE = ROW_BYTES / sizeof(T);
-  const int nk = K / KE;
-  // Pipeline per slab kt (stage kt&1), fragments double-buffered over k16 steps:
-  //   steps 0..2: read the next step's fragments, 16 MFMAs on the current ones;
-  //   then wait for this wave's loads of slab kt+1 and for its last LDS reads, one
-  //   barrier (slab kt+1 is in LDS for everyone; stage kt&1 is free), start the
-  //   loads of slab kt+2 into stage kt&1, read slab kt+1's first fragments;
-  //   step 3: 16 MFMAs, which hide that barrier and those reads.
+  const int nk = K / KE;   // >= NSTAGE: K >= 256, KE <= 64 and NSTAGE <= 4 for 128-byte rows
+
+  // Pipeline per slab kt (stage kt % NSTAGE), fragments double-buffered over the
+  // k16 steps: steps 0..KSTEPS-2 read the next step's fragments, then run 16 MFMAs;
+  // then wait for this wave's loads of slab kt+1 and its own LDS reads, one barrier
+  // (slab kt+1 is in LDS for everyone, and nobody reads slab kt any more), start the
+  // loads of slab kt+NSTAGE into slab kt's stage, read slab kt+1's first fragments;
+  // the last step's 16 MFMAs hide that barrier and those reads.  A slab's loads
+  // have NSTAGE-1 slabs of MFMA work to land.
   frag_t fa[2][4], fb[2][4];
   auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
@@ -245,29 +318,58 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
 #pragma unroll
       for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
   };
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-  __syncthreads();
-  if (nk > 1) issue(1, 1);
-  read_frags(smem, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const unsigned char* sP = smem + (kt & 1) * STAGE_BYTES;
+#if MO_GEMM_LOAD_PATH == 0
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
+  for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(sidx, sidx);   // nk >= NSTAGE
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 1)));
+  __syncthreads();
+#else
+  load_regs(0);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  write_lds(0);
+  load_regs(1);                                                   // nk >= 2
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));           // lgkmcnt(0) only
+  __syncthreads();
+#endif
+  read_frags(smem, 0, fa[0], fb[0]);
+  int stage = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char* sP = smem + stage * STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS - 1; ++kk) {
       read_frags(sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       mfma_step(fa[kk & 1], fb[kk & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    const int next = (stage + 1 == NSTAGE) ? 0 : stage + 1;
+    // The block below runs on every slab, the last one included (where it reads
+    // stale, unused fragments), so that the wait counters the last step's MFMAs
+    // see do not depend on the path taken.  Slab kt+1 must have landed; slabs
+    // kt+2 .. kt+NSTAGE-1 may still be in flight.
+#if MO_GEMM_LOAD_PATH == 0
+    if (kt + NSTAGE - 1 < nk)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    __syncthreads();
+    if (kt + NSTAGE < nk) issue(kt + NSTAGE, stage);
+#else
+    // slab kt+1 is in registers: store it to the other stage (free since the
+    // previous barrier), then make it visible; start loading slab kt+2
     if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-      __syncthreads();
-      if (kt + 2 < nk) issue(kt + 2, kt & 1);
-      read_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, fa[0], fb[0]);
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      write_lds(next);
     }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    __syncthreads();
+    if (kt + 2 < nk) load_regs(kt + 2);
+#endif
+    read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa[1], fb[1]);
+    mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
+    stage = next;
   }
 
   // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
@@ -277,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   // symmetric) for POLY and X^T[j][ib..] for APPLY.  Loads are issued a whole
   // sub-block row (16 vectors) at a time before any of them is used.
   typedef typename Vec4<T>::type v4_t;
-  const int64_t ldt = d.mp;
+  const int64_t ldt = d.ldm;
   if (MODE == GM_SYRK || MODE == GM_POLY) {
     T* C = static_cast<T*>(MODE == GM_SYRK ? d.A : d.B);
     const T* Ain = static_cast<const T*>(d.A);
@@ -328,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     T* X = static_cast<T*>(d.X);
     const T* XTc = static_cast<const T*>(d.XT[parity]);
     T* XTn = static_cast<T*>(d.XT[parity ^ 1]);
-    const int64_t ldx = d.np;
+    const int64_t ldx = d.ldx;
     TO* out = static_cast<TO*>(d.out);
     const int m = d.m, n = d.n;
 #pragma unroll

@@ -105,9 +105,13 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.np = static_cast<int32_t>(round_up(d.n, GEMM_TILE));
     d.vec_ok = (aligned16(d.grad) && aligned16(d.mom) && aligned16(d.out) && (mt.cols % 4 == 0)) ? 1 : 0;
     d.scale_slot = k;
-    const size_t xb = size_t(d.mp) * size_t(d.np) * es, ab = size_t(d.mp) * size_t(d.mp) * es;
+    d.ldx = d.np + static_cast<int32_t>(LD_PAD_BYTES / es);
+    d.ldm = d.mp + static_cast<int32_t>(LD_PAD_BYTES / es);
+    const size_t xb = size_t(d.mp) * size_t(d.ldx) * es;    // X: mp rows of ldx
+    const size_t tb = size_t(d.np) * size_t(d.ldm) * es;    // X^T: np rows of ldm
+    const size_t ab = size_t(d.mp) * size_t(d.ldm) * es;    // A, B: mp rows of ldm
     // the GEMM addresses each operand buffer with 32-bit byte offsets
-    if (xb > size_t(0x7fffffff))
+    if (xb > size_t(0x7fffffff) || tb > size_t(0x7fffffff))
       return fail(MO_ERR_UNSUPPORTED, "matrix " + std::to_string(order[k]) +
                                           ": padded operand exceeds 2 GiB (min(rows,cols) * max(rows,cols))");
     auto take = [&](size_t nb) {
@@ -116,8 +120,8 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
       return p;
     };
     d.X = take(xb);
-    d.XT[0] = take(xb);
-    d.XT[1] = take(xb);
+    d.XT[0] = take(tb);
+    d.XT[1] = take(tb);
     d.A = take(ab);
     d.B = take(ab);
     const int64_t tm = d.mp / GEMM_TILE, tn = d.np / GEMM_TILE;
