@@ -13,9 +13,11 @@
 // All workspace dims are multiples of 256, zero-padded, so the main loop needs no
 // bounds checks; only the final write to the caller's buffer is clipped.
 //
-// Tiling (gfx950, wave64): 256x256 block tile, 4 waves in 2x2, each wave owns a
-// 128x128 sub-tile = 4x4 MFMA 32x32 blocks (256 fp32 accumulators per lane, held in
-// AGPRs).  The k-loop streams 128-byte row slabs (64 bf16 or 32 fp32 of k) of both
+// Tiling (gfx950, wave64): 256x256 block tile; NWAVES = 8 waves in a 2 x 4 grid,
+// each owning a 128 x 64 sub-tile = 4 x 2 MFMA 32x32 blocks (128 fp32 accumulators
+// per lane), two waves per SIMD so that twice as many operand loads are in flight
+// as with 4 waves of 128 x 128 (the operand stream into LDS, not the MFMA rate, is
+// what bounds this kernel).  The k-loop streams 128-byte row slabs (64 bf16 or 32 fp32 of k) of both
 // operands straight from HBM/L2 into LDS with 16-byte buffer loads that write LDS
 // directly (no register staging), through a 2-stage ring: the loads of slab t+1
 // are in flight while slab t is multiplied.  LDS rows are 128 bytes with the 16-byte
@@ -52,12 +54,20 @@ constexpr int NSTAGE = MO_GEMM_STAGES;
 constexpr int OPERAND_BYTES = GT * ROW_BYTES;
 constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;         // P and Q
 constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
+#ifndef MO_GEMM_WAVES
+#define MO_GEMM_WAVES 8
+#endif
+constexpr int NWAVES = MO_GEMM_WAVES;                  // 4 or 8
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int WAVES_N = NWAVES / 2;                    // wave grid: 2 x WAVES_N
+constexpr int WAVE_N = GT / WAVES_N;                   // columns per wave: 128 or 64
+constexpr int NB = WAVE_N / 32;                        // 32-column MFMA blocks per wave
 constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;        // rows one 1 KiB wave load fills
-constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / 4;  // per wave, per slab
+constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / NWAVES;  // per wave, per slab
 constexpr int INST_PER_SLAB = 2 * INST_PER_OPERAND;
 static_assert(GEMM_LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
 static_assert(MO_GEMM_LOAD_PATH == 0 || NSTAGE == 2, "the register path uses two LDS stages");
-constexpr int NPASS = OPERAND_BYTES / (256 * 16);      // 16-byte loads per thread, per operand
+constexpr int NPASS = OPERAND_BYTES / (NTHREADS * 16);  // 16-byte loads per thread, per operand
 static_assert(NSTAGE * (ROW_BYTES / 2) <= 256, "the ring must not be deeper than the shortest K (256)");
 static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
 
@@ -177,7 +187,8 @@ template <> __device__ inline void store4<float>(float* p, float v0, float v1, f
 }
 
 template <typename T, int MODE, typename TO>
-__global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
+void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
                                                     int parity, float ca, float cb, float cc) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave / WAVES_N) * 128, wn = (wave % WAVES_N) * WAVE_N;
 
   // Direct-to-LDS loads: wave w, instruction q fills ROWS_PER_INST rows starting at
   // ROWS_PER_INST*(4q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   uint32_t vP[INST_PER_OPERAND], vQ[INST_PER_OPERAND];
 #pragma unroll
   for (int q = 0; q < INST_PER_OPERAND; ++q) {
-    const int row = ROWS_PER_INST * (4 * q + wave) + lane / CHUNKS;
+    const int row = ROWS_PER_INST * (NWAVES * q + wave) + lane / CHUNKS;
     const int c = (lane % CHUNKS) ^ swz(row);
     vP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
     vQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
@@ -238,11 +249,12 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     unsigned char* base = smem + stage * STAGE_BYTES + wave * 1024;
 #pragma unroll
     for (int q = 0; q < INST_PER_OPERAND; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * 4096), 16, vP[q], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * NWAVES * 1024), 16, vP[q], soff, 0,
+                                               0);
 #pragma unroll
     for (int q = 0; q < INST_PER_OPERAND; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * 4096), 16, vQ[q],
-                                               soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * NWAVES * 1024), 16,
+                                               vQ[q], soff, 0, 0);
   };
 
   // Register path: thread t moves logical chunk t % CHUNKS of rows
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   uint32_t gP[NPASS], gQ[NPASS], lOff[NPASS];
 #pragma unroll
   for (int q = 0; q < NPASS; ++q) {
-    const int row = (256 / CHUNKS) * q + tid / CHUNKS;
+    const int row = (NTHREADS / CHUNKS) * q + tid / CHUNKS;
     const int c = tid % CHUNKS;
     gP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
     gQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
@@ -274,21 +286,20 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   // fragment read offsets (row part), per sub-block
-  int rowA[4], rowB[4];
+  int rowA[4], rowB[NB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    rowA[a] = wm + a * 32 + l32;
-    rowB[a] = wn + a * 32 + l32;
-  }
+  for (int a = 0; a < 4; ++a) rowA[a] = wm + a * 32 + l32;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rowB[b] = wn + b * 32 + l32;
 
   typedef typename Mfma<T>::frag frag_t;
   const int KE = ROW_BYTES / sizeof(T);
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
   // loads of slab kt+NSTAGE into slab kt's stage, read slab kt+1's first fragments;
   // the last step's 16 MFMAs hide that barrier and those reads.  A slab's loads
   // have NSTAGE-1 slabs of MFMA work to land.
-  frag_t fa[2][4], fb[2][4];
+  frag_t fa[2][4], fb[2][NB];
   auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
     const int c = 2 * kk + half;
@@ -309,14 +320,14 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     for (int a = 0; a < 4; ++a)
       A[a] = *reinterpret_cast<const frag_t*>(sP + rowA[a] * ROW_BYTES + ((c ^ swz(rowA[a])) << 4));
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
       B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
   };
   auto mfma_step = [&](const frag_t* A, const frag_t* B) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
+      for (int b = 0; b < NB; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
   };
 #if MO_GEMM_LOAD_PATH == 0
 #pragma unroll
@@ -386,10 +397,10 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     const bool diag = (ti == tj);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      v4_t e[4][4];
+      v4_t e[NB][4];
       if (MODE == GM_POLY) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
           }
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
@@ -435,9 +446,9 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
     const int m = d.m, n = d.n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      v4_t e[4][4];
+      v4_t e[NB][4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(256, 1) void k_ns_gemm(const MatDesc* __restrict__ 
           e[b][g] = *reinterpret_cast<const v4_t*>(XTc + static_cast<int64_t>(j) * ldt + ib);
         }
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;

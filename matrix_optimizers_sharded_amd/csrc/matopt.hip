@@ -232,20 +232,20 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
   for (int t = 0; t < ns.iters; ++t) {
     const int parity = t & 1;
     MO_TRY(launch(PK_SYRK, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(plan.total[KIND_SYRK]), dim3(256), 0, stream,
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(plan.total[KIND_SYRK]), dim3(NTHREADS), 0, stream,
                          dd, count, parity, 0.f, 0.f, 0.f);
     }));
     MO_TRY(launch(PK_POLY, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(plan.total[KIND_POLY]), dim3(256), 0, stream,
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(plan.total[KIND_POLY]), dim3(NTHREADS), 0, stream,
                          dd, count, parity, 0.f, ns.b, ns.c);
     }));
     const bool last = (t + 1 == ns.iters);
     MO_TRY(launch(PK_APPLY, stream, [&] {
       if (last)
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(plan.total[KIND_APPLY]), dim3(256), 0,
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0,
                            stream, dd, count, parity, ns.a, 0.f, 0.f);
       else
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(plan.total[KIND_APPLY]), dim3(256), 0, stream,
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0, stream,
                            dd, count, parity, ns.a, 0.f, 0.f);
     }));
   }
