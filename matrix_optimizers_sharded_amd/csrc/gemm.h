@@ -42,8 +42,10 @@ constexpr int GT = GEMM_TILE;          // 256
 #ifndef MO_GEMM_STAGES
 #define MO_GEMM_STAGES 2
 #endif
-// operand path into LDS: 0 = direct-to-LDS buffer loads, 1 = buffer loads into
-// registers one slab ahead, then ds_write_b128 (2 LDS stages)
+// operand path into LDS: 0 = direct-to-LDS buffer loads; 1 = buffer loads into
+// registers one slab ahead, then ds_write_b128; 2 = two register batches, so the
+// loads of slabs t+3 and t+4 are in flight while slab t is multiplied (both
+// register paths use 2 LDS stages)
 #ifndef MO_GEMM_LOAD_PATH
 #define MO_GEMM_LOAD_PATH 0
 #endif
@@ -236,53 +238,57 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
       const_cast<T*>(P), 0, static_cast<int>(rowsP * static_cast<uint32_t>(ldp) * esz), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(Q), 0, static_cast<int>(rowsQ * static_cast<uint32_t>(ldq) * esz), RSRC_FLAGS);
-  uint32_t vP[INST_PER_OPERAND], vQ[INST_PER_OPERAND];
-#pragma unroll
-  for (int q = 0; q < INST_PER_OPERAND; ++q) {
-    const int row = ROWS_PER_INST * (NWAVES * q + wave) + lane / CHUNKS;
-    const int c = (lane % CHUNKS) ^ swz(row);
-    vP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
-    vQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
-  }
+  // Rows advance by ROWS_PER_INST * NWAVES between a wave's instructions, a multiple
+  // of 16, which leaves the swizzle unchanged: one base offset per operand plus a
+  // uniform stride per instruction.
+  const int row0 = ROWS_PER_INST * wave + lane / CHUNKS;
+  const uint32_t vP0 = static_cast<uint32_t>(i0 + row0) * static_cast<uint32_t>(ldp) * esz +
+                       (((lane % CHUNKS) ^ swz(row0)) << 4);
+  const uint32_t vQ0 = static_cast<uint32_t>(j0 + row0) * static_cast<uint32_t>(ldq) * esz +
+                       (((lane % CHUNKS) ^ swz(row0)) << 4);
+  const uint32_t vPs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * static_cast<uint32_t>(ldp) * esz;
+  const uint32_t vQs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * static_cast<uint32_t>(ldq) * esz;
   auto issue = [&](int kt, int stage) {
     const int soff = kt * ROW_BYTES;
     unsigned char* base = smem + stage * STAGE_BYTES + wave * 1024;
 #pragma unroll
     for (int q = 0; q < INST_PER_OPERAND; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * NWAVES * 1024), 16, vP[q], soff, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * NWAVES * 1024), 16, vP0 + q * vPs,
+                                               soff, 0, 0);
 #pragma unroll
     for (int q = 0; q < INST_PER_OPERAND; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * NWAVES * 1024), 16,
-                                               vQ[q], soff, 0, 0);
+                                               vQ0 + q * vQs, soff, 0, 0);
   };
 
   // Register path: thread t moves logical chunk t % CHUNKS of rows
-  // (256 / CHUNKS) * q + t / CHUNKS; the LDS position applies the same swizzle.
+  // (NTHREADS / CHUNKS) * q + t / CHUNKS; that row step is a multiple of 16, so the
+  // swizzle, and with it the LDS offset pattern, is the same for every pass.
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  uint32_t gP[NPASS], gQ[NPASS], lOff[NPASS];
+  constexpr int PASS_ROWS = NTHREADS / CHUNKS;
+  static_assert(PASS_ROWS % 16 == 0, "pass row step must keep the swizzle");
+  const int prow0 = tid / CHUNKS, pc = tid % CHUNKS;
+  const uint32_t gP0 = static_cast<uint32_t>(i0 + prow0) * static_cast<uint32_t>(ldp) * esz + pc * 16;
+  const uint32_t gQ0 = static_cast<uint32_t>(j0 + prow0) * static_cast<uint32_t>(ldq) * esz + pc * 16;
+  const uint32_t gPs = static_cast<uint32_t>(PASS_ROWS) * static_cast<uint32_t>(ldp) * esz;
+  const uint32_t gQs = static_cast<uint32_t>(PASS_ROWS) * static_cast<uint32_t>(ldq) * esz;
+  const uint32_t lOff0 = prow0 * ROW_BYTES + ((pc ^ swz(prow0)) << 4);
+  constexpr int NSETS = MO_GEMM_LOAD_PATH == 2 ? 2 : 1;
+  constexpr int NREG = MO_GEMM_LOAD_PATH ? NPASS : 0;
+  u32x4_t rgP[NSETS][NREG > 0 ? NREG : 1], rgQ[NSETS][NREG > 0 ? NREG : 1];
+  auto load_regs = [&](int set, int kt) {
 #pragma unroll
-  for (int q = 0; q < NPASS; ++q) {
-    const int row = (NTHREADS / CHUNKS) * q + tid / CHUNKS;
-    const int c = tid % CHUNKS;
-    gP[q] = static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz + c * 16;
-    gQ[q] = static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz + c * 16;
-    lOff[q] = row * ROW_BYTES + ((c ^ swz(row)) << 4);
-  }
-  u32x4_t rgP[MO_GEMM_LOAD_PATH ? NPASS : 1], rgQ[MO_GEMM_LOAD_PATH ? NPASS : 1];
-  auto load_regs = [&](int kt) {
-#pragma unroll
-    for (int q = 0; q < (MO_GEMM_LOAD_PATH ? NPASS : 0); ++q) {
-      rgP[q] = __builtin_amdgcn_raw_buffer_load_b128(rP, gP[q], kt * ROW_BYTES, 0);
-      rgQ[q] = __builtin_amdgcn_raw_buffer_load_b128(rQ, gQ[q], kt * ROW_BYTES, 0);
+    for (int q = 0; q < NREG; ++q) {
+      rgP[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rP, gP0 + q * gPs, kt * ROW_BYTES, 0);
+      rgQ[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rQ, gQ0 + q * gQs, kt * ROW_BYTES, 0);
     }
   };
-  auto write_lds = [&](int stage) {
+  auto write_lds = [&](int set, int stage) {
     unsigned char* base = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int q = 0; q < (MO_GEMM_LOAD_PATH ? NPASS : 0); ++q) {
-      *reinterpret_cast<u32x4_t*>(base + lOff[q]) = rgP[q];
-      *reinterpret_cast<u32x4_t*>(base + OPERAND_BYTES + lOff[q]) = rgQ[q];
+    for (int q = 0; q < NREG; ++q) {
+      *reinterpret_cast<u32x4_t*>(base + lOff0 + q * PASS_ROWS * ROW_BYTES) = rgP[set][q];
+      *reinterpret_cast<u32x4_t*>(base + OPERAND_BYTES + lOff0 + q * PASS_ROWS * ROW_BYTES) = rgQ[set][q];
     }
   };
 
@@ -334,12 +340,24 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
   for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(sidx, sidx);   // nk >= NSTAGE
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 1)));
   __syncthreads();
-#else
-  load_regs(0);
+#elif MO_GEMM_LOAD_PATH == 1
+  load_regs(0, 0);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  write_lds(0);
-  load_regs(1);                                                   // nk >= 2
+  write_lds(0, 0);
+  load_regs(0, 1);                                                // nk >= 2
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));           // lgkmcnt(0) only
+  __syncthreads();
+#else
+  // slabs 0 and 1 into LDS, slabs 2 and 3 left loading into the two register sets
+  load_regs(0, 0);
+  load_regs(1, 1);                                                // nk >= 4
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));
+  write_lds(0, 0);
+  load_regs(0, 2);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));
+  write_lds(1, 1);
+  load_regs(1, 3);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * NPASS));           // lgkmcnt(0) only
   __syncthreads();
 #endif
   read_frags(smem, 0, fa[0], fb[0]);
@@ -365,21 +383,43 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     __syncthreads();
     if (kt + NSTAGE < nk) issue(kt + NSTAGE, stage);
-#else
+#elif MO_GEMM_LOAD_PATH == 1
     // slab kt+1 is in registers: store it to the other stage (free since the
     // previous barrier), then make it visible; start loading slab kt+2
     if (kt + 1 < nk) {
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-      write_lds(next);
+      write_lds(0, next);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     __syncthreads();
-    if (kt + 2 < nk) load_regs(kt + 2);
+    if (kt + 2 < nk) load_regs(0, kt + 2);
+#else
+    // everyone has read slab kt and slab kt+1 is in LDS (written one slab ago,
+    // fenced by this barrier); slab kt+2 sits in register set kt&1
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0x3f));              // lgkmcnt(0) only
+    __syncthreads();
 #endif
     read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
+#if MO_GEMM_LOAD_PATH == 2
+    // stage kt&1 is free: move slab kt+2 (register set kt&1, loaded two slabs ago)
+    // into it, then reuse the set for slab kt+4
+    if (kt + 2 < nk) {
+      if (kt + 3 < nk)
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS) | (15 << 8));   // set kt&1 landed
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0) | (15 << 8));
+      if (kt & 1) {
+        write_lds(1, stage);
+        if (kt + 4 < nk) load_regs(1, kt + 4);
+      } else {
+        write_lds(0, stage);
+        if (kt + 4 < nk) load_regs(0, kt + 4);
+      }
+    }
+#endif
     stage = next;
   }
 
