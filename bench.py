@@ -52,6 +52,17 @@ def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
     return {"momentum_sumsq": mom, "prep_operand": numel * (src + 2 * compute_bytes)}
 
 
+def traffic_of(kind, workload):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 counter summary for
+    this workload, or None if there is none or the kernel sources changed since."""
+    from matrix_optimizers_sharded_amd.profsummary import read_traffic, source_hash
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    val, h = read_traffic(path, kind)
+    if val is None or h != source_hash():
+        return None
+    return val
+
+
 def cpu_baseline(wid, iters):
     """The fp64 oracle on a bounded sample of the workload, on the host cores."""
     import numpy as np
@@ -96,6 +107,8 @@ def main():
     ap.add_argument("--workload", default="7b-class", choices=sorted(NAMES))
     ap.add_argument("--compute", default=None, choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the owner-local step needs "
@@ -115,6 +128,14 @@ def main():
     shapes = w.shapes
     print(f"[bench] workload {w.name}: {w.count} matrices, {w.numel / 1e9:.3f} G params, compute {compute_name}",
           file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] 1 GiB calibration copy done", file=sys.stderr, flush=True)
 
     ws = mo.Workspace(dev)
     if wid == 5:
@@ -196,12 +217,12 @@ def main():
         _, pl_ms, work = per_launch(dom)
         achieved = work / (pl_ms / 1e3) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_of(dom, w.name)}
     elif dom in hbm:
         _, pl_ms, work = per_launch(dom)
         achieved = work / (pl_ms / 1e3) / 1e9
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_of(dom, w.name)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,160 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+    python -m matrix_optimizers_sharded_amd.profsummary trace <stats.csv> <out.txt> --cmd "<command>"
+    python -m matrix_optimizers_sharded_amd.profsummary pmc <fetch.csv> <write.csv> <out.txt> \
+        --cmd-fetch "<command>" --cmd-write "<command>" [--copy-bytes N]
+
+`trace` summarises a `--kernel-trace --stats` run (calls and mean duration per
+kernel kind).  `pmc` summarises two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
+command that also performs one plain device copy of --copy-bytes (bench.py
+--calibrate-copy): each counter is scaled by what it reads for that copy, giving
+HBM bytes per dispatch.  Both record a hash of the library's kernel sources; the
+benchmark reports the traffic figure only while that hash still matches.
+"""
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+KINDS = [
+    (re.compile(r"k_ns_gemm.*Li0E"), "ns_syrk"),
+    (re.compile(r"k_ns_gemm.*Li1E"), "ns_poly"),
+    (re.compile(r"k_ns_gemm.*Li[23]E"), "ns_apply"),
+    (re.compile(r"k_momentum_sumsq"), "momentum_sumsq"),
+    (re.compile(r"k_prep_operand"), "prep_operand"),
+    (re.compile(r"k_norm_scale"), "norm_scale"),
+    (re.compile(r"k_scaled_copy"), "scaled_copy"),
+    (re.compile(r"k_sign_pack"), "sign_pack"),
+    (re.compile(r"k_sign_vote"), "sign_vote"),
+    (re.compile(r"__amd_rocclr_copyBuffer"), "device_copy"),
+]
+
+
+def source_hash():
+    """sha256 over the library's kernel sources (csrc/*.h, csrc/*.hip), in name order."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*.h")) + glob.glob(os.path.join(PKG, "csrc", "*.hip"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kind_of(name):
+    for pat, kind in KINDS:
+        if pat.search(name):
+            return kind
+    return None
+
+
+def summarize_trace(stats_csv, cmd):
+    calls = collections.Counter()
+    total = collections.Counter()
+    for r in csv.DictReader(open(stats_csv)):
+        k = kind_of(r["Name"])
+        if k is None:
+            continue
+        calls[k] += int(r["Calls"])
+        total[k] += float(r["TotalDurationNs"])
+    lines = [
+        "# rocprofv3 --kernel-trace --stats summary, per kernel kind",
+        f"# command: {cmd}",
+        f"source_sha256 = {source_hash()}",
+        f"{'kind':<16} {'calls':>7} {'mean_ms':>10} {'total_ms':>10}",
+    ]
+    for k in sorted(calls, key=lambda k: -total[k]):
+        lines.append(f"{k:<16} {calls[k]:>7} {total[k] / calls[k] / 1e6:>10.4f} {total[k] / 1e6:>10.3f}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_by_kind(path, counter):
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = kind_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        vals[k].append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes):
+    fetch = _counter_by_kind(fetch_csv, "FETCH_SIZE")
+    write = _counter_by_kind(write_csv, "WRITE_SIZE")
+    if "device_copy" not in fetch or "device_copy" not in write:
+        raise SystemExit("no device copy dispatch found for calibration")
+    # the runtime may split the calibration copy into several dispatches: sum them
+    cf, cw = sum(fetch["device_copy"]), sum(write["device_copy"])
+    fs = copy_bytes / (cf * 1024.0)
+    ws = copy_bytes / (cw * 1024.0)
+    lines = [
+        "# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per",
+        "# dispatch), each scaled by what the same counter reads for one plain device copy of",
+        f"# {copy_bytes} bytes in the same run",
+        f"# command (fetch): {cmd_fetch}",
+        f"# command (write): {cmd_write}",
+        f"source_sha256 = {source_hash()}",
+        f"copy_bytes = {copy_bytes}",
+        f"copy_fetch_kib = {cf:.1f}",
+        f"copy_write_kib = {cw:.1f}",
+        f"fetch_scale = {fs:.4f}",
+        f"write_scale = {ws:.4f}",
+        f"{'kind':<16} {'dispatches':>10} {'fetch_kib':>14} {'write_kib':>14} {'hbm_bytes_per_launch':>22}",
+    ]
+    for k in sorted(set(fetch) & set(write)):
+        if k == "device_copy":
+            continue
+        f = sum(fetch[k]) / len(fetch[k])
+        w = sum(write[k]) / len(write[k])
+        b = f * 1024.0 * fs + w * 1024.0 * ws
+        lines.append(f"{k:<16} {len(fetch[k]):>10} {f:>14.1f} {w:>14.1f} {b:>22.4e}")
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path, kind):
+    """(bytes per launch, source hash) for `kind` from a pmc summary, or (None, None)."""
+    if not os.path.exists(path):
+        return None, None
+    h, val = None, None
+    for line in open(path):
+        if line.startswith("source_sha256"):
+            h = line.split("=")[1].strip()
+        parts = line.split()
+        if parts and parts[0] == kind and len(parts) == 5:
+            val = float(parts[4])
+    return val, h
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("fetch_csv")
+    p.add_argument("write_csv")
+    p.add_argument("out")
+    p.add_argument("--cmd-fetch", required=True)
+    p.add_argument("--cmd-write", required=True)
+    p.add_argument("--copy-bytes", type=int, default=1 << 30)
+    a = ap.parse_args()
+    if a.mode == "trace":
+        text = summarize_trace(a.stats_csv, a.cmd)
+    else:
+        text = summarize_pmc(a.fetch_csv, a.write_csv, a.cmd_fetch, a.cmd_write, a.copy_bytes)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
