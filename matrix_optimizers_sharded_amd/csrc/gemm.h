@@ -4,12 +4,15 @@
 // k-contiguous rows:
 //   SYRK   A  = X X^T         P = Q = X (rows of X, k over n); upper tiles only,
 //                             each off-diagonal tile also stored mirrored
-//   POLY   B  = bA + c A A    P = Q = A (A symmetric, so A A = A A^T); upper tiles,
-//                             mirrored; b*A in the epilogue reads the same rounded A
-//   APPLY  X' = aX + B X      P = B, Q = X^T (the kernel keeps X^T as a second
-//                             copy so this is k-contiguous too); the epilogue
-//                             reads X, writes X' in place and X'^T to the other
-//                             ping-pong buffer, or the final U to the caller.
+//   POLY   B' = aI + bA + c A A   P = Q = A (A symmetric, so A A = A A^T); upper
+//                             tiles, mirrored; b*A in the epilogue reads the same
+//                             rounded A, and a is added on the diagonal (rows < m)
+//   APPLY  X' = B' X = aX + (bA + cA^2) X   P = B', Q = X^T (the kernel keeps X^T
+//                             as a second copy so this is k-contiguous too); the
+//                             epilogue only stores: X' in place and X'^T to the
+//                             other ping-pong buffer, or the final U to the caller.
+// Folding a into B' removes every epilogue read from the largest product; it
+// rounds a + B_ii to the compute dtype once instead of rounding B_ii.
 // All workspace dims are multiples of 256, zero-padded, so the main loop needs no
 // bounds checks; only the final write to the caller's buffer is clipped.
 //
@@ -458,7 +461,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             v[t] = acc[a][b][4 * g + t];
-            if (MODE == GM_POLY) v[t] = cb * to_f32(e[b][g][t]) + cc * v[t];
+            if (MODE == GM_POLY) {
+              v[t] = cb * to_f32(e[b][g][t]) + cc * v[t];
+              if (diag && ib + t == j && j < d.m) v[t] += ca;
+            }
           }
           if (!diag) {
 #pragma unroll
@@ -479,22 +485,12 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
     }
   } else {
     T* X = static_cast<T*>(d.X);
-    const T* XTc = static_cast<const T*>(d.XT[parity]);
     T* XTn = static_cast<T*>(d.XT[parity ^ 1]);
     const int64_t ldx = d.ldx;
     TO* out = static_cast<TO*>(d.out);
     const int m = d.m, n = d.n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      v4_t e[NB][4];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-          const int j = j0 + wn + b * 32 + l32;
-          e[b][g] = *reinterpret_cast<const v4_t*>(XTc + static_cast<int64_t>(j) * ldt + ib);
-        }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -503,7 +499,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
           const int j = j0 + wn + b * 32 + l32;
           float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = ca * to_f32(e[b][g][t]) + acc[a][b][4 * g + t];
+          for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
           if (MODE == GM_APPLY) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) X[static_cast<int64_t>(ib + t) * ldx + j] = from_f32<T>(v[t]);

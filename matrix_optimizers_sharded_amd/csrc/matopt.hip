@@ -7,6 +7,7 @@
 //   k_norm_scale       per-matrix 1 / (||M||_F + eps)                    (tiny)
 //   k_prep_operand     scaled, oriented, zero-padded X0 and X0^T         (HBM)
 //   iters x { k_ns_gemm<SYRK>, k_ns_gemm<POLY>, k_ns_gemm<APPLY> }       (MFMA)
+//             A = X X^T,  B' = aI + bA + cA^2,  X <- B' X
 // Each launch covers every matrix of the batch (grouped launch); blocks find their
 // matrix by binary search over the table, which is sorted by decreasing size so
 // the longest tiles start first.
@@ -237,16 +238,16 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
     }));
     MO_TRY(launch(PK_POLY, stream, [&] {
       hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(plan.total[KIND_POLY]), dim3(NTHREADS), 0, stream,
-                         dd, count, parity, 0.f, ns.b, ns.c);
+                         dd, count, parity, ns.a, ns.b, ns.c);
     }));
     const bool last = (t + 1 == ns.iters);
     MO_TRY(launch(PK_APPLY, stream, [&] {
       if (last)
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0,
-                           stream, dd, count, parity, ns.a, 0.f, 0.f);
+                           stream, dd, count, parity, 0.f, 0.f, 0.f);
       else
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0, stream,
-                           dd, count, parity, ns.a, 0.f, 0.f);
+                           dd, count, parity, 0.f, 0.f, 0.f);
     }));
   }
   return MO_OK;
