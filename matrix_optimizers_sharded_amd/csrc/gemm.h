@@ -52,6 +52,15 @@ constexpr int GT = GEMM_TILE;          // 256
 #ifndef MO_GEMM_LOAD_PATH
 #define MO_GEMM_LOAD_PATH 0
 #endif
+// 1: one slab beyond the loads in flight, touch every 128-byte line of the next
+// operand slab with a 4-byte load (one lane per line, into a 256-byte scratch area
+// of LDS), so that slab is already in L2 when its real loads are issued
+#ifndef MO_GEMM_L2_PREFETCH
+#define MO_GEMM_L2_PREFETCH 0
+#endif
+#ifndef MO_GEMM_PF_DIST
+#define MO_GEMM_PF_DIST 1        // slabs beyond the furthest slab being loaded
+#endif
 constexpr int ROW_BYTES = MO_GEMM_SLAB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
 constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
@@ -75,6 +84,8 @@ static_assert(MO_GEMM_LOAD_PATH == 0 || NSTAGE == 2, "the register path uses two
 constexpr int NPASS = OPERAND_BYTES / (NTHREADS * 16);  // 16-byte loads per thread, per operand
 static_assert(NSTAGE * (ROW_BYTES / 2) <= 256, "the ring must not be deeper than the shortest K (256)");
 static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
+constexpr int PF_INST = MO_GEMM_L2_PREFETCH ? (2 * GT) / (64 * NWAVES) : 0;   // per wave, per slab
+constexpr int PF_LDS = 256;                                                   // scratch bytes
 
 // raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
 constexpr int RSRC_FLAGS = 0x00020000;
@@ -195,7 +206,7 @@ template <typename T, int MODE, typename TO>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
 void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
                                                     int parity, float ca, float cb, float cc) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES + PF_LDS];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
   const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
   const MatDesc& d = descs[find_desc(descs, count, kind, item)];
@@ -226,7 +237,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
   const int i0 = ti * GT, j0 = tj * GT;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = (wave / WAVES_N) * 128, wn = (wave % WAVES_N) * WAVE_N;
 
@@ -295,6 +306,24 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
     }
   };
 
+  // L2 prefetch: lane g = 64 * (NWAVES * q + wave) + lane of the block touches line
+  // g of the next slab (P rows 0..255, then Q rows 0..255) at 128-byte granularity
+  auto prefetch = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < PF_INST; ++q) {
+      const int blk = NWAVES * q + wave;           // wave-uniform: P lines, then Q lines
+      const int row = (64 * blk + lane) & (GT - 1);
+      if (64 * blk < GT)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(smem + GEMM_LDS_BYTES), 4,
+                                                 static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz,
+                                                 kt * ROW_BYTES, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(smem + GEMM_LDS_BYTES), 4,
+                                                 static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz,
+                                                 kt * ROW_BYTES, 0, 0);
+    }
+  };
+
   f32x16_t acc[4][NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -341,7 +370,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
 #if MO_GEMM_LOAD_PATH == 0
 #pragma unroll
   for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(sidx, sidx);   // nk >= NSTAGE
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 1)));
+#pragma unroll
+  for (int dd = 0; dd < MO_GEMM_PF_DIST; ++dd)
+    if (PF_INST && NSTAGE + dd < nk) prefetch(NSTAGE + dd);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   __syncthreads();
 #elif MO_GEMM_LOAD_PATH == 1
   load_regs(0, 0);
@@ -380,12 +412,17 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
     // see do not depend on the path taken.  Slab kt+1 must have landed; slabs
     // kt+2 .. kt+NSTAGE-1 may still be in flight.
 #if MO_GEMM_LOAD_PATH == 0
-    if (kt + NSTAGE - 1 < nk)
+    // (issued after slab kt+1, per wave: the loads of slabs kt+2 .. kt+NSTAGE-1 and
+    // the prefetch of slab kt+NSTAGE)
+    if (kt + NSTAGE < nk)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2) + PF_INST));
+    else if (kt + NSTAGE - 1 < nk)
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2)));
     else
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     __syncthreads();
     if (kt + NSTAGE < nk) issue(kt + NSTAGE, stage);
+    if (PF_INST && kt + NSTAGE + MO_GEMM_PF_DIST < nk) prefetch(kt + NSTAGE + MO_GEMM_PF_DIST);
 #elif MO_GEMM_LOAD_PATH == 1
     // slab kt+1 is in registers: store it to the other stage (free since the
     // previous barrier), then make it visible; start loading slab kt+2
