@@ -52,6 +52,39 @@ def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
     return {"momentum_sumsq": mom, "prep_operand": numel * (src + 2 * compute_bytes)}
 
 
+def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):
+    """HBM roofline of the Sign-Muon kernels at a size where bandwidth, not launch
+    latency, decides: sign_pack reads 4 B and writes 1/8 B per element (fp32 input);
+    sign_vote reads workers/8 B and writes 1/8 B per element."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12345)
+    u = torch.randn(numel, generator=gen, device=dev, dtype=torch.float32)
+    nwords = (numel + 31) // 32
+    packed = torch.empty((workers, nwords), dtype=torch.int32, device=dev)
+    out = torch.empty(nwords, dtype=torch.int32, device=dev)
+    for i in range(workers):
+        mo.sign_pack(u, packed[i])
+    mo.sign_vote(packed, numel, out_packed=out)
+    torch.cuda.synchronize()
+    mo.profile_begin()
+    for _ in range(reps):
+        mo.sign_pack(u, packed[0])
+        mo.sign_vote(packed, numel, out_packed=out)
+    torch.cuda.synchronize()
+    k = mo.profile_end()
+    pack_ms = k["sign_pack"][1] / k["sign_pack"][0]
+    vote_ms = k["sign_vote"][1] / k["sign_vote"][0]
+    pack_b = numel * (4 + 1 / 8)
+    vote_b = numel * (workers + 1) / 8
+    res = {"numel": numel, "workers": workers,
+           "sign_pack": {"ms": round(pack_ms, 4), "gbs": round(pack_b / pack_ms / 1e6, 1),
+                         "frac_hbm": round(pack_b / pack_ms / 1e6 / PEAK_HBM_GBS, 4)},
+           "sign_vote": {"ms": round(vote_ms, 4), "gbs": round(vote_b / vote_ms / 1e6, 1),
+                         "frac_hbm": round(vote_b / vote_ms / 1e6 / PEAK_HBM_GBS, 4)}}
+    del u, packed, out
+    return res
+
+
 def traffic_of(kind, workload):
     """HBM bytes per launch of `kind` from the committed rocprofv3 counter summary for
     this workload, or None if there is none or the kernel sources changed since."""
@@ -107,6 +140,9 @@ def main():
     ap.add_argument("--workload", default="7b-class", choices=sorted(NAMES))
     ap.add_argument("--compute", default=None, choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sign-tail-numel", type=int, default=None,
+                    help="also time sign_pack (fp32 input) and an 8-worker sign_vote on this many elements "
+                         "(default: 2^28 for the sign-vote workload, off otherwise)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -224,6 +260,11 @@ def main():
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_of(dom, w.name)}
 
+    sign_tail = None
+    tail_numel = args.sign_tail_numel if args.sign_tail_numel is not None else (1 << 28 if wid == 5 else 0)
+    if tail_numel:
+        sign_tail = measure_sign_tail(mo, torch, dev, tail_numel)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -251,6 +292,7 @@ def main():
         "kernels": breakdown,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sign_tail": sign_tail,
     }
     print(json.dumps(line), flush=True)
 

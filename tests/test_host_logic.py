@@ -1,0 +1,125 @@
+"""Host-side logic that needs no GPU: workload definitions and seeded inputs, the
+benchmark's work accounting, the profile summariser, and the rule that the product
+path never touches the oracle."""
+
+import ast
+import os
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+from matrix_optimizers_sharded_amd import workloads as W
+from matrix_optimizers_sharded_amd import profsummary
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "matrix_optimizers_sharded_amd")
+
+
+def test_workload_sizes():
+    assert W.WORKLOADS[1].numel == 256 * 128
+    assert W.WORKLOADS[2].count == 72 and W.WORKLOADS[2].numel == 84934656
+    assert W.WORKLOADS[3].count == 112 and W.WORKLOADS[3].numel == 822083584
+    assert W.WORKLOADS[4].count == 224 and W.WORKLOADS[4].numel == 6476005376
+    assert W.WORKLOADS[5].count == 8 and W.WORKLOADS[5].shapes[0] == (4096, 4096)
+    # listing order is layer-major: layer 0's seven matrices first
+    assert W.WORKLOADS[4].shapes[:7] == [(4096, 4096)] * 4 + [(4096, 11008)] * 2 + [(11008, 4096)]
+
+
+def test_bf16_cast_is_round_to_nearest_even():
+    import torch
+    x = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * np.float32(1e-2)
+    # include exact ties: values halfway between two bf16 numbers
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(W.f32_to_bf16_bits(x), want)
+    np.testing.assert_array_equal(W.bf16_bits_to_f32(want), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_host_inputs_are_seeded_and_shaped():
+    a = W.host_matrix(2, 5)
+    b = W.host_matrix(2, 5)
+    assert a["shape"] == (3072, 768) and a["grad"].shape == (3072, 768)
+    np.testing.assert_array_equal(a["grad"], b["grad"])
+    np.testing.assert_array_equal(a["mom"], b["mom"])
+    assert a["grad_bits"].dtype == np.uint16
+    np.testing.assert_array_equal(W.bf16_bits_to_f32(a["grad_bits"]), a["grad"])
+    c = W.host_matrix(2, 6)
+    assert not np.array_equal(a["grad"][:768], c["grad"][:768])
+    assert abs(float(a["grad"].std()) - 0.02) < 1e-3
+
+
+def test_heavy_tail_rows():
+    rows = W.heavy_tail_rows(3, 6, 5632)
+    assert len(rows) == 56 and len(set(rows.tolist())) == 56
+    d = W.host_matrix(3, 6)
+    norms = np.linalg.norm(d["grad"], axis=1)
+    mask = np.zeros(5632, bool)
+    mask[rows] = True
+    assert norms[mask].min() > 5 * norms[~mask].max() / 2
+
+
+def test_bench_flop_accounting_matches_oracle_formula():
+    import bench
+    shapes = W.WORKLOADS[4].shapes
+    f = bench.ns_flops(shapes, 5)
+    total = sum(oracle.ns_polynomial_flops(r, c, 5) for r, c in shapes)
+    assert sum(f.values()) == total
+    assert abs(total - 4.7485e14) / 4.7485e14 < 1e-3
+    b = bench.hbm_bytes(shapes, 2, 2)
+    assert b["momentum_sumsq"] == W.WORKLOADS[4].numel * 10
+    assert b["prep_operand"] == W.WORKLOADS[4].numel * 8
+
+
+def test_profsummary_round_trip(tmp_path):
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    hdr = "Kernel_Name,Counter_Name,Counter_Value\n"
+    fetch.write_text(hdr + textwrap.dedent("""\
+        __amd_rocclr_copyBuffer,FETCH_SIZE,524288
+        _ZN2mo9k_ns_gemmIDF16bLi2EDF16bEEvPKNS_7MatDescEiifff,FETCH_SIZE,1000
+        _ZN2mo9k_ns_gemmIDF16bLi3EDF16bEEvPKNS_7MatDescEiifff,FETCH_SIZE,3000
+        """))
+    write.write_text(hdr + textwrap.dedent("""\
+        __amd_rocclr_copyBuffer,WRITE_SIZE,1048576
+        _ZN2mo9k_ns_gemmIDF16bLi2EDF16bEEvPKNS_7MatDescEiifff,WRITE_SIZE,100
+        _ZN2mo9k_ns_gemmIDF16bLi3EDF16bEEvPKNS_7MatDescEiifff,WRITE_SIZE,300
+        """))
+    text = profsummary.summarize_pmc(str(fetch), str(write), "f", "w", 1 << 30)
+    out = tmp_path / "s.txt"
+    out.write_text(text)
+    val, h = profsummary.read_traffic(str(out), "ns_apply")
+    # fetch scale 2, write scale 1; mean of the two APPLY dispatches
+    assert val == pytest.approx((2000 * 1024 * 2.0) + (200 * 1024 * 1.0))
+    assert h == profsummary.source_hash()
+
+
+def _imports(path):
+    tree = ast.parse(open(path).read())
+    names = set()
+    for node in ast.walk(tree):
+        if isinstance(node, ast.Import):
+            names.update(a.name.split(".")[0] for a in node.names)
+        elif isinstance(node, ast.ImportFrom) and node.module:
+            names.add(node.module.split(".")[0])
+    return names
+
+
+def test_product_code_never_imports_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            p = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                assert "oracle" not in _imports(p), p
+            if f.endswith((".hip", ".h")):
+                assert "oracle" not in open(p).read().lower(), p
+    # bench.py may use it only inside its CPU-baseline function
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    for node in ast.walk(tree):
+        if isinstance(node, ast.FunctionDef) and node.name != "cpu_baseline":
+            for sub in ast.walk(node):
+                if isinstance(sub, (ast.Import, ast.ImportFrom)):
+                    mods = [a.name for a in sub.names] if isinstance(sub, ast.Import) else [sub.module or ""]
+                    assert not any(m.split(".")[0] == "oracle" for m in mods), node.name
