@@ -36,7 +36,7 @@ enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3 };
 
 constexpr int GT = GEMM_TILE;          // 256
 
-// k-slab geometry: each operand row of a slab is ROW_BYTES (64: 32 bf16 / 16 fp32 of
+// k-slab geometry: each operand row of a slab is ROW_BYTES (128: 64 bf16 / 32 fp32 of
 // k), and NSTAGE slabs are in flight in an LDS ring, so the loads of slab t+NSTAGE-1
 // overlap the MFMAs of slabs t .. t+NSTAGE-2.
 #ifndef MO_GEMM_SLAB_BYTES
@@ -44,22 +44,6 @@ constexpr int GT = GEMM_TILE;          // 256
 #endif
 #ifndef MO_GEMM_STAGES
 #define MO_GEMM_STAGES 2
-#endif
-// operand path into LDS: 0 = direct-to-LDS buffer loads; 1 = buffer loads into
-// registers one slab ahead, then ds_write_b128; 2 = two register batches, so the
-// loads of slabs t+3 and t+4 are in flight while slab t is multiplied (both
-// register paths use 2 LDS stages)
-#ifndef MO_GEMM_LOAD_PATH
-#define MO_GEMM_LOAD_PATH 0
-#endif
-// 1: one slab beyond the loads in flight, touch every 128-byte line of the next
-// operand slab with a 4-byte load (one lane per line, into a 256-byte scratch area
-// of LDS), so that slab is already in L2 when its real loads are issued
-#ifndef MO_GEMM_L2_PREFETCH
-#define MO_GEMM_L2_PREFETCH 0
-#endif
-#ifndef MO_GEMM_PF_DIST
-#define MO_GEMM_PF_DIST 1        // slabs beyond the furthest slab being loaded
 #endif
 constexpr int ROW_BYTES = MO_GEMM_SLAB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
@@ -71,7 +55,7 @@ constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
 #ifndef MO_GEMM_WAVES
 #define MO_GEMM_WAVES 8
 #endif
-constexpr int NWAVES = MO_GEMM_WAVES;                  // 4 or 8
+constexpr int NWAVES = MO_GEMM_WAVES;                  // 8 (4 builds and is slower)
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WAVES_N = NWAVES / 2;                    // wave grid: 2 x WAVES_N
 constexpr int WAVE_N = GT / WAVES_N;                   // columns per wave: 128 or 64
@@ -80,12 +64,8 @@ constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;        // rows one 1 KiB wave lo
 constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / NWAVES;  // per wave, per slab
 constexpr int INST_PER_SLAB = 2 * INST_PER_OPERAND;
 static_assert(GEMM_LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
-static_assert(MO_GEMM_LOAD_PATH == 0 || NSTAGE == 2, "the register path uses two LDS stages");
-constexpr int NPASS = OPERAND_BYTES / (NTHREADS * 16);  // 16-byte loads per thread, per operand
 static_assert(NSTAGE * (ROW_BYTES / 2) <= 256, "the ring must not be deeper than the shortest K (256)");
 static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
-constexpr int PF_INST = MO_GEMM_L2_PREFETCH ? (2 * GT) / (64 * NWAVES) : 0;   // per wave, per slab
-constexpr int PF_LDS = 256;                                                   // scratch bytes
 
 // raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
 constexpr int RSRC_FLAGS = 0x00020000;
@@ -206,7 +186,7 @@ template <typename T, int MODE, typename TO>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
 void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
                                                     int parity, float ca, float cb, float cc) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES + PF_LDS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
   const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
   const MatDesc& d = descs[find_desc(descs, count, kind, item)];
@@ -242,7 +222,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
   const int wm = (wave / WAVES_N) * 128, wn = (wave % WAVES_N) * WAVE_N;
 
   // Direct-to-LDS loads: wave w, instruction q fills ROWS_PER_INST rows starting at
-  // ROWS_PER_INST*(4q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
+  // ROWS_PER_INST*(NWAVES*q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
   // row + l/CHUNKS, physical chunk l%CHUNKS); the lane fetches the logical chunk
   // that the swizzle stores there.
   const uint32_t esz = sizeof(T);
@@ -273,55 +253,6 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
     for (int q = 0; q < INST_PER_OPERAND; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * NWAVES * 1024), 16,
                                                vQ0 + q * vQs, soff, 0, 0);
-  };
-
-  // Register path: thread t moves logical chunk t % CHUNKS of rows
-  // (NTHREADS / CHUNKS) * q + t / CHUNKS; that row step is a multiple of 16, so the
-  // swizzle, and with it the LDS offset pattern, is the same for every pass.
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  constexpr int PASS_ROWS = NTHREADS / CHUNKS;
-  static_assert(PASS_ROWS % 16 == 0, "pass row step must keep the swizzle");
-  const int prow0 = tid / CHUNKS, pc = tid % CHUNKS;
-  const uint32_t gP0 = static_cast<uint32_t>(i0 + prow0) * static_cast<uint32_t>(ldp) * esz + pc * 16;
-  const uint32_t gQ0 = static_cast<uint32_t>(j0 + prow0) * static_cast<uint32_t>(ldq) * esz + pc * 16;
-  const uint32_t gPs = static_cast<uint32_t>(PASS_ROWS) * static_cast<uint32_t>(ldp) * esz;
-  const uint32_t gQs = static_cast<uint32_t>(PASS_ROWS) * static_cast<uint32_t>(ldq) * esz;
-  const uint32_t lOff0 = prow0 * ROW_BYTES + ((pc ^ swz(prow0)) << 4);
-  constexpr int NSETS = MO_GEMM_LOAD_PATH == 2 ? 2 : 1;
-  constexpr int NREG = MO_GEMM_LOAD_PATH ? NPASS : 0;
-  u32x4_t rgP[NSETS][NREG > 0 ? NREG : 1], rgQ[NSETS][NREG > 0 ? NREG : 1];
-  auto load_regs = [&](int set, int kt) {
-#pragma unroll
-    for (int q = 0; q < NREG; ++q) {
-      rgP[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rP, gP0 + q * gPs, kt * ROW_BYTES, 0);
-      rgQ[set][q] = __builtin_amdgcn_raw_buffer_load_b128(rQ, gQ0 + q * gQs, kt * ROW_BYTES, 0);
-    }
-  };
-  auto write_lds = [&](int set, int stage) {
-    unsigned char* base = smem + stage * STAGE_BYTES;
-#pragma unroll
-    for (int q = 0; q < NREG; ++q) {
-      *reinterpret_cast<u32x4_t*>(base + lOff0 + q * PASS_ROWS * ROW_BYTES) = rgP[set][q];
-      *reinterpret_cast<u32x4_t*>(base + OPERAND_BYTES + lOff0 + q * PASS_ROWS * ROW_BYTES) = rgQ[set][q];
-    }
-  };
-
-  // L2 prefetch: lane g = 64 * (NWAVES * q + wave) + lane of the block touches line
-  // g of the next slab (P rows 0..255, then Q rows 0..255) at 128-byte granularity
-  auto prefetch = [&](int kt) {
-#pragma unroll
-    for (int q = 0; q < PF_INST; ++q) {
-      const int blk = NWAVES * q + wave;           // wave-uniform: P lines, then Q lines
-      const int row = (64 * blk + lane) & (GT - 1);
-      if (64 * blk < GT)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(smem + GEMM_LDS_BYTES), 4,
-                                                 static_cast<uint32_t>(i0 + row) * static_cast<uint32_t>(ldp) * esz,
-                                                 kt * ROW_BYTES, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(smem + GEMM_LDS_BYTES), 4,
-                                                 static_cast<uint32_t>(j0 + row) * static_cast<uint32_t>(ldq) * esz,
-                                                 kt * ROW_BYTES, 0, 0);
-    }
   };
 
   f32x16_t acc[4][NB];
@@ -367,34 +298,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
 #pragma unroll
       for (int b = 0; b < NB; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
   };
-#if MO_GEMM_LOAD_PATH == 0
 #pragma unroll
   for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(sidx, sidx);   // nk >= NSTAGE
-#pragma unroll
-  for (int dd = 0; dd < MO_GEMM_PF_DIST; ++dd)
-    if (PF_INST && NSTAGE + dd < nk) prefetch(NSTAGE + dd);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 1)));
   __syncthreads();
-#elif MO_GEMM_LOAD_PATH == 1
-  load_regs(0, 0);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  write_lds(0, 0);
-  load_regs(0, 1);                                                // nk >= 2
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));           // lgkmcnt(0) only
-  __syncthreads();
-#else
-  // slabs 0 and 1 into LDS, slabs 2 and 3 left loading into the two register sets
-  load_regs(0, 0);
-  load_regs(1, 1);                                                // nk >= 4
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));
-  write_lds(0, 0);
-  load_regs(0, 2);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS));
-  write_lds(1, 1);
-  load_regs(1, 3);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * NPASS));           // lgkmcnt(0) only
-  __syncthreads();
-#endif
   read_frags(smem, 0, fa[0], fb[0]);
   int stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
@@ -411,55 +318,16 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
     // stale, unused fragments), so that the wait counters the last step's MFMAs
     // see do not depend on the path taken.  Slab kt+1 must have landed; slabs
     // kt+2 .. kt+NSTAGE-1 may still be in flight.
-#if MO_GEMM_LOAD_PATH == 0
-    // (issued after slab kt+1, per wave: the loads of slabs kt+2 .. kt+NSTAGE-1 and
-    // the prefetch of slab kt+NSTAGE)
-    if (kt + NSTAGE < nk)
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2) + PF_INST));
-    else if (kt + NSTAGE - 1 < nk)
+    if (kt + NSTAGE - 1 < nk)
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2)));
     else
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     __syncthreads();
     if (kt + NSTAGE < nk) issue(kt + NSTAGE, stage);
-    if (PF_INST && kt + NSTAGE + MO_GEMM_PF_DIST < nk) prefetch(kt + NSTAGE + MO_GEMM_PF_DIST);
-#elif MO_GEMM_LOAD_PATH == 1
-    // slab kt+1 is in registers: store it to the other stage (free since the
-    // previous barrier), then make it visible; start loading slab kt+2
-    if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-      write_lds(0, next);
-    }
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-    __syncthreads();
-    if (kt + 2 < nk) load_regs(0, kt + 2);
-#else
-    // everyone has read slab kt and slab kt+1 is in LDS (written one slab ago,
-    // fenced by this barrier); slab kt+2 sits in register set kt&1
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0x3f));              // lgkmcnt(0) only
-    __syncthreads();
-#endif
     read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-#if MO_GEMM_LOAD_PATH == 2
-    // stage kt&1 is free: move slab kt+2 (register set kt&1, loaded two slabs ago)
-    // into it, then reuse the set for slab kt+4
-    if (kt + 2 < nk) {
-      if (kt + 3 < nk)
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NPASS) | (15 << 8));   // set kt&1 landed
-      else
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0) | (15 << 8));
-      if (kt & 1) {
-        write_lds(1, stage);
-        if (kt + 4 < nk) load_regs(1, kt + 4);
-      } else {
-        write_lds(0, stage);
-        if (kt + 4 < nk) load_regs(0, kt + 4);
-      }
-    }
-#endif
     stage = next;
   }
 
