@@ -52,6 +52,13 @@ struct MatDesc {
   int32_t pad_[3];
 };
 
+// Global-address-space view of a device pointer.  Accesses through it compile to
+// global_* instructions, which count only against vmcnt; through a generic pointer
+// the compiler emits flat_* instructions, which count against lgkmcnt as well, so
+// the next wait for an LDS read would also wait for every one of them to finish.
+template <typename T> using gptr = __attribute__((address_space(1))) T*;
+template <typename T> __device__ inline gptr<T> global(T* p) { return (gptr<T>)p; }
+
 __device__ inline int find_desc(const MatDesc* __restrict__ d, int count, int kind, int64_t item) {
   int lo = 0, hi = count - 1;
   while (lo < hi) {

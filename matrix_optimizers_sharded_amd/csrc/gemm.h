@@ -63,8 +63,10 @@ constexpr int NB = WAVE_N / 32;                        // 32-column MFMA blocks 
 constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;        // rows one 1 KiB wave load fills
 constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / NWAVES;  // per wave, per slab
 constexpr int INST_PER_SLAB = 2 * INST_PER_OPERAND;
-static_assert(GEMM_LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
-static_assert(NSTAGE * (ROW_BYTES / 2) <= 256, "the ring must not be deeper than the shortest K (256)");
+static_assert(GEMM_LDS_BYTES + NWAVES * 4096 <= 160 * 1024, "LDS ring and staging exceed 160 KiB");
+// the shortest K is 256: a tile has at least 512 / ROW_BYTES slabs (bf16), and the
+// persistent ring needs NSTAGE + 2 of them per tile
+static_assert(512 / ROW_BYTES >= NSTAGE + 2, "ring too deep for K = 256");
 static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
 
 // raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
@@ -79,6 +81,77 @@ __device__ inline int swz(int r) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, size in bytes, flags.
+__device__ inline i32x4_t buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4_t r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = RSRC_FLAGS;
+  return r;
+}
+
+// Four 16-byte-per-lane loads from one buffer straight into LDS: load q writes
+// lds[q] + 16 * lane from byte voff[q] + soff of the buffer.  Written as inline asm
+// so that the compiler's wait-count pass does not track them: that pass cannot tell
+// which ring stage they write and would otherwise wait for them before every LDS
+// read.  The ring's own explicit waits cover these loads.  M0 (the LDS base of a
+// load) is saved and restored, so the compiler's view of it stays valid; every
+// operand is made uniform first so that it is an SGPR.
+__device__ inline void load_lds16x4(i32x4_t rsrc, const uint32_t (&lds)[4], const uint32_t (&voff)[4],
+                                    uint32_t soff) {
+  i32x4_t r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = __builtin_amdgcn_readfirstlane(rsrc[c]);
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds[0]), l1 = __builtin_amdgcn_readfirstlane(lds[1]);
+  const uint32_t l2 = __builtin_amdgcn_readfirstlane(lds[2]), l3 = __builtin_amdgcn_readfirstlane(lds[3]);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %10 offen lds\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %10 offen lds\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %9, %10 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %9, %10 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(r),
+        "s"(so)
+      : "memory");
+}
+// The same for two loads from each of two buffers (P then Q) in one block.
+__device__ inline void load_lds16_2x2(i32x4_t rsrc_p, i32x4_t rsrc_q, const uint32_t (&lds)[4],
+                                      const uint32_t (&voff)[4], uint32_t soff) {
+  i32x4_t rp, rq;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    rp[c] = __builtin_amdgcn_readfirstlane(rsrc_p[c]);
+    rq[c] = __builtin_amdgcn_readfirstlane(rsrc_q[c]);
+  }
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds[0]), l1 = __builtin_amdgcn_readfirstlane(lds[1]);
+  const uint32_t l2 = __builtin_amdgcn_readfirstlane(lds[2]), l3 = __builtin_amdgcn_readfirstlane(lds[3]);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %11 offen lds\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %11 offen lds\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %10, %11 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %10, %11 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rp),
+        "s"(rq), "s"(so)
+      : "memory");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt = N (bits 3:0 and 15:14), expcnt = 7
 // (no wait), lgkmcnt = 0
@@ -167,101 +240,135 @@ __device__ inline int64_t xcd_remap(int64_t b, int64_t total) {
   return (k / G) * (8 * G) + x * G + (k % G);
 }
 
+// element at a byte offset from a global base pointer
+template <typename V, typename T>
+__device__ inline gptr<V> at(gptr<T> base, uint32_t byte_off) {
+  typedef __attribute__((address_space(1))) unsigned char* bytes_t;
+  return (gptr<V>)((bytes_t)base + byte_off);
+}
+
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16_t> { typedef bf16x4_t type; };
 template <> struct Vec4<float> { typedef f32x4_t type; };
 
 template <typename T>
-__device__ inline void store4(T* p, float v0, float v1, float v2, float v3);
-template <> __device__ inline void store4<bf16_t>(bf16_t* p, float v0, float v1, float v2, float v3) {
-  bf16x4_t v = {static_cast<bf16_t>(v0), static_cast<bf16_t>(v1), static_cast<bf16_t>(v2),
-                static_cast<bf16_t>(v3)};
-  *reinterpret_cast<bf16x4_t*>(p) = v;
-}
-template <> __device__ inline void store4<float>(float* p, float v0, float v1, float v2, float v3) {
-  *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v0, v1, v2, v3};
+__device__ inline void store4(gptr<T> p, float v0, float v1, float v2, float v3) {
+  typedef typename Vec4<T>::type v4_t;
+  const v4_t v = {from_f32<T>(v0), from_f32<T>(v1), from_f32<T>(v2), from_f32<T>(v3)};
+  *reinterpret_cast<gptr<v4_t>>(p) = v;
 }
 
+// One tile's operand stream: buffer resources over P and Q and this lane's byte
+// offsets of its first rows, plus where the tile sits.
+struct TileRef {
+  int di, ti, tj, nk;   // descriptor index, tile row and column, k slabs
+  i32x4_t rP, rQ;
+  uint32_t vP0, vQ0, vPs, vQs;
+};
+
+// Persistent kernel: the grid holds at most one block per CU, and block b walks the
+// work items b, b + G, b + 2G, ... of the remapped order (G = gridDim.x, a multiple
+// of 8 whenever a block gets more than one item, so a block keeps to its XCD's share
+// of that order).  The operand ring runs across tile boundaries: the last NSTAGE
+// slabs of a tile start the loads of the next tile's first slabs, so those land while
+// this tile finishes and writes its epilogue, and no tile pays a cold start.  (A
+// shared work queue fed by an atomic counter measured about 1% slower.)
 template <typename T, int MODE, typename TO>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
-void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
-                                                    int parity, float ca, float cb, float cc) {
+void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int parity, float ca, float cb,
+               float cc) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
+  // per-wave 4 KiB epilogue staging slabs
+  __shared__ __attribute__((aligned(16))) unsigned char staging[NWAVES * 4096];
   constexpr int kind = (MODE == GM_SYRK) ? KIND_SYRK : (MODE == GM_POLY) ? KIND_POLY : KIND_APPLY;
-  const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : static_cast<int64_t>(blockIdx.x);
-  const MatDesc& d = descs[find_desc(descs, count, kind, item)];
-  const int64_t local = item - d.begin[kind];
-
-  int ti, tj;
-  const T* P;
-  const T* Q;
-  int64_t ldp, ldq;
-  int K;
-  if (MODE == GM_SYRK) {
-    upper_tile(local, d.mp / GT, ti, tj);
-    P = Q = static_cast<const T*>(d.X);
-    ldp = ldq = d.ldx;
-    K = d.np;
-  } else if (MODE == GM_POLY) {
-    upper_tile(local, d.mp / GT, ti, tj);
-    P = Q = static_cast<const T*>(d.A);
-    ldp = ldq = d.ldm;
-    K = d.mp;
-  } else {
-    rect_tile(local, d.mp / GT, d.np / GT, ti, tj);
-    P = static_cast<const T*>(d.B);
-    Q = static_cast<const T*>(d.XT[parity]);
-    ldp = ldq = d.ldm;
-    K = d.mp;
-  }
-  const int i0 = ti * GT, j0 = tj * GT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = (wave / WAVES_N) * 128, wn = (wave % WAVES_N) * WAVE_N;
+  const uint32_t esz = sizeof(T);
 
   // Direct-to-LDS loads: wave w, instruction q fills ROWS_PER_INST rows starting at
   // ROWS_PER_INST*(NWAVES*q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
   // row + l/CHUNKS, physical chunk l%CHUNKS); the lane fetches the logical chunk
-  // that the swizzle stores there.
-  const uint32_t esz = sizeof(T);
-  const uint32_t rowsP = d.mp;   // X, A and B all have mp rows
-  const uint32_t rowsQ = (MODE == GM_APPLY || MODE == GM_APPLY_FINAL) ? d.np : d.mp;
-  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(P), 0, static_cast<int>(rowsP * static_cast<uint32_t>(ldp) * esz), RSRC_FLAGS);
-  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(Q), 0, static_cast<int>(rowsQ * static_cast<uint32_t>(ldq) * esz), RSRC_FLAGS);
-  // Rows advance by ROWS_PER_INST * NWAVES between a wave's instructions, a multiple
-  // of 16, which leaves the swizzle unchanged: one base offset per operand plus a
-  // uniform stride per instruction.
+  // that the swizzle stores there.  Rows advance by ROWS_PER_INST * NWAVES between a
+  // wave's instructions, a multiple of 16, which leaves the swizzle unchanged: one
+  // base offset per operand plus a uniform stride per instruction.
   const int row0 = ROWS_PER_INST * wave + lane / CHUNKS;
-  const uint32_t vP0 = static_cast<uint32_t>(i0 + row0) * static_cast<uint32_t>(ldp) * esz +
-                       (((lane % CHUNKS) ^ swz(row0)) << 4);
-  const uint32_t vQ0 = static_cast<uint32_t>(j0 + row0) * static_cast<uint32_t>(ldq) * esz +
-                       (((lane % CHUNKS) ^ swz(row0)) << 4);
-  const uint32_t vPs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * static_cast<uint32_t>(ldp) * esz;
-  const uint32_t vQs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * static_cast<uint32_t>(ldq) * esz;
-  auto issue = [&](int kt, int stage) {
-    const int soff = kt * ROW_BYTES;
-    unsigned char* base = smem + stage * STAGE_BYTES + wave * 1024;
+  const uint32_t lane_chunk = ((lane % CHUNKS) ^ swz(row0)) << 4;
+
+  auto setup = [&](int64_t v, TileRef& t) {
+    const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(v, total) : v;
+    const int di = __builtin_amdgcn_readfirstlane(find_desc(descs, count, kind, item));
+    const MatDesc* d = descs + di;
+    const int64_t local = item - d->begin[kind];
+    const T* P;
+    const T* Q;
+    int64_t ld;
+    uint32_t rowsQ;
+    int K;
+    if (MODE == GM_SYRK) {
+      upper_tile(local, d->mp / GT, t.ti, t.tj);
+      P = Q = static_cast<const T*>(d->X);
+      ld = d->ldx;
+      rowsQ = d->mp;
+      K = d->np;
+    } else if (MODE == GM_POLY) {
+      upper_tile(local, d->mp / GT, t.ti, t.tj);
+      P = Q = static_cast<const T*>(d->A);
+      ld = d->ldm;
+      rowsQ = d->mp;
+      K = d->mp;
+    } else {
+      rect_tile(local, d->mp / GT, d->np / GT, t.ti, t.tj);
+      P = static_cast<const T*>(d->B);
+      Q = static_cast<const T*>(d->XT[parity]);
+      ld = d->ldm;
+      rowsQ = d->np;
+      K = d->mp;
+    }
+    t.di = di;
+    t.nk = K / (ROW_BYTES / static_cast<int>(sizeof(T)));   // >= NSTAGE + 2: K >= 256
+    const uint32_t pitch = static_cast<uint32_t>(ld) * esz;
+    // X, A and B all have mp rows; X^T has np
+    t.rP = buffer_rsrc(P, d->mp * pitch);
+    t.rQ = buffer_rsrc(Q, rowsQ * pitch);
+    t.vP0 = static_cast<uint32_t>(t.ti * GT + row0) * pitch + lane_chunk;
+    t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * pitch + lane_chunk;
+    t.vPs = t.vQs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * pitch;
+  };
+  static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND == 4, "loads per operand per wave: 2 or 4");
+  auto issue = [&](const TileRef& t, int kt, int stage) {
+    const uint32_t soff = kt * ROW_BYTES;
+    const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
+    if (INST_PER_OPERAND == 2) {
+      const uint32_t l[4] = {base, base + NWAVES * 1024, base + OPERAND_BYTES, base + OPERAND_BYTES + NWAVES * 1024};
+      const uint32_t v[4] = {t.vP0, t.vP0 + t.vPs, t.vQ0, t.vQ0 + t.vQs};
+      load_lds16_2x2(t.rP, t.rQ, l, v, soff);
+    } else {
+      uint32_t lp[4], lq[4], vp[4], vq[4];
 #pragma unroll
-    for (int q = 0; q < INST_PER_OPERAND; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + q * NWAVES * 1024), 16, vP0 + q * vPs,
-                                               soff, 0, 0);
-#pragma unroll
-    for (int q = 0; q < INST_PER_OPERAND; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(base + OPERAND_BYTES + q * NWAVES * 1024), 16,
-                                               vQ0 + q * vQs, soff, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        lp[q] = base + q * NWAVES * 1024;
+        lq[q] = lp[q] + OPERAND_BYTES;
+        vp[q] = t.vP0 + q * t.vPs;
+        vq[q] = t.vQ0 + q * t.vQs;
+      }
+      load_lds16x4(t.rP, lp, vp, soff);
+      load_lds16x4(t.rQ, lq, vq, soff);
+    }
   };
 
+
   f32x16_t acc[4][NB];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  };
 
   // fragment read offsets (row part), per sub-block
   int rowA[4], rowB[NB];
@@ -271,16 +378,16 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
   for (int b = 0; b < NB; ++b) rowB[b] = wn + b * 32 + l32;
 
   typedef typename Mfma<T>::frag frag_t;
-  const int KE = ROW_BYTES / sizeof(T);
-  const int nk = K / KE;   // >= NSTAGE: K >= 256, KE <= 64 and NSTAGE <= 4 for 128-byte rows
-
   // Pipeline per slab kt (stage kt % NSTAGE), fragments double-buffered over the
   // k16 steps: steps 0..KSTEPS-2 read the next step's fragments, then run 16 MFMAs;
-  // then wait for this wave's loads of slab kt+1 and its own LDS reads, one barrier
-  // (slab kt+1 is in LDS for everyone, and nobody reads slab kt any more), start the
-  // loads of slab kt+NSTAGE into slab kt's stage, read slab kt+1's first fragments;
-  // the last step's 16 MFMAs hide that barrier and those reads.  A slab's loads
-  // have NSTAGE-1 slabs of MFMA work to land.
+  // then wait until this wave's loads of slab kt+1 have landed (later slabs may stay
+  // in flight) and its own LDS reads are done, one barrier (slab kt+1 is in LDS for
+  // everyone, and nobody reads slab kt any more), start the loads of slab
+  // kt+NSTAGE (of this tile or the next) into slab kt's stage, read slab kt+1's
+  // first fragments; the last step's 16 MFMAs hide that barrier and those reads.
+  // The waits count loads only: buffer loads complete in issue order, so "at most
+  // n outstanding", with n the loads issued after slab kt+1's, means slab kt+1 is
+  // in, whatever stores or atomics are also in flight.
   frag_t fa[2][4], fb[2][NB];
   auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
@@ -298,101 +405,187 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
 #pragma unroll
       for (int b = 0; b < NB; ++b) Mfma<T>::mma(acc[a][b], A[a], B[b]);
   };
+
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth 2..5");
+  auto wait_loads = [&](int n) {   // at most n slabs' loads of this wave still in flight
+    if (NSTAGE > 4 && n >= 3)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * INST_PER_SLAB));
+    else if (NSTAGE > 3 && n >= 2)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * INST_PER_SLAB));
+    else if (NSTAGE > 2 && n >= 1)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  };
+
+  const int64_t G = gridDim.x;
+  int64_t v = blockIdx.x;   // < total: the grid never exceeds the item count
+  TileRef cur, nxt;
+  setup(v, cur);
+  bool has_next = v + G < total;
+  if (has_next) setup(v + G, nxt);
+
+  // prologue: slabs 0..NSTAGE-1 of the first tile (every tile has more slabs)
 #pragma unroll
-  for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(sidx, sidx);   // nk >= NSTAGE
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 1)));
+  for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(cur, sidx, sidx);
+  wait_loads(NSTAGE - 1);
   __syncthreads();
   read_frags(smem, 0, fa[0], fb[0]);
   int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const unsigned char* sP = smem + stage * STAGE_BYTES;
+  for (;;) {
+    zero_acc();
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      const unsigned char* sP = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS - 1; ++kk) {
-      read_frags(sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      for (int kk = 0; kk < KSTEPS - 1; ++kk) {
+        read_frags(sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(fa[kk & 1], fb[kk & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int next = (stage + 1 == NSTAGE) ? 0 : stage + 1;
+      // loads issued after slab kt+1's: slabs kt+2 .. kt+NSTAGE-1, those past this
+      // tile only if there is a next one.  On the block's very last slab the reads
+      // below fetch stale, unused fragments.
+      wait_loads(has_next ? NSTAGE - 2 : min(NSTAGE - 2, cur.nk - kt - 2));
+      __syncthreads();
+      // one issue site for both cases (see load_lds16x4)
+      {
+        const int ks = kt + NSTAGE;
+        const bool own = ks < cur.nk;
+        if (own || has_next) issue(own ? cur : nxt, own ? ks : ks - cur.nk, stage);
+      }
+      read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step(fa[kk & 1], fb[kk & 1]);
+      mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
+      stage = next;
     }
-    const int next = (stage + 1 == NSTAGE) ? 0 : stage + 1;
-    // The block below runs on every slab, the last one included (where it reads
-    // stale, unused fragments), so that the wait counters the last step's MFMAs
-    // see do not depend on the path taken.  Slab kt+1 must have landed; slabs
-    // kt+2 .. kt+NSTAGE-1 may still be in flight.
-    if (kt + NSTAGE - 1 < nk)
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB * (NSTAGE - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-    __syncthreads();
-    if (kt + NSTAGE < nk) issue(kt + NSTAGE, stage);
-    read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-    stage = next;
-  }
 
+    {
+    // a uniform index, so the descriptor comes in through scalar loads, which no
+    // vmcnt wait covers (a vector load here would wait for the ring's loads too)
+    const MatDesc& d = descs[__builtin_amdgcn_readfirstlane(cur.di)];
+    const int ti = cur.ti, tj = cur.tj;
+    const int i0 = ti * GT, j0 = tj * GT;
   // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
-  // ib..ib+3 of one column j per register group g.  Values the epilogue needs at
-  // [ib..ib+3][j] are read as one vector from a transposed copy: A[j][ib..] (A is
-  // symmetric) for POLY and X^T[j][ib..] for APPLY.  Loads are issued a whole
-  // sub-block row (16 vectors) at a time before any of them is used.
+  // ib..ib+3 of one column j per register group g.
+  //
+  // Row-major results (X', or C = A or B') are stored straight from the registers:
+  // one instruction writes 64 contiguous bytes of each of 8 rows.  The transposed
+  // copies (X'^T, the mirror tile of C) would leave the registers as 8 or 16 bytes
+  // per row per instruction, i.e. 8 partial writes per 128-byte line, and L2 write
+  // traffic of that shape slows everyone's operand loads.  They go through this
+  // wave's 4 KiB LDS staging slab instead: a round puts 32 columns j x 128 bytes of
+  // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
+  // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
+  // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
   typedef typename Vec4<T>::type v4_t;
   const int64_t ldt = d.ldm;
-  if (MODE == GM_SYRK || MODE == GM_POLY) {
-    T* C = static_cast<T*>(MODE == GM_SYRK ? d.A : d.B);
-    const T* Ain = static_cast<const T*>(d.A);
-    const bool diag = (ti == tj);
+  if (MODE != GM_APPLY_FINAL) {
+    constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128-byte line
+    gptr<T> Cr, Ct;   // row-major and transposed destinations
+    int64_t ldr;
+    if (MODE == GM_APPLY) {
+      Cr = global(static_cast<T*>(d.X));
+      ldr = d.ldx;
+      Ct = global(static_cast<T*>(d.XT[parity ^ 1]));
+    } else {
+      Cr = Ct = global(static_cast<T*>(MODE == GM_SYRK ? d.A : d.B));
+      ldr = ldt;
+    }
+    const gptr<const T> Ain = global(static_cast<const T*>(d.A));
+    const bool diag = MODE != GM_APPLY && ti == tj;
+    // Every workspace buffer is below 2 GiB: element addresses are a uniform base
+    // plus a 32-bit byte offset, one VGPR per address.
+    constexpr uint32_t ES = sizeof(T);
+    const uint32_t ldr_b = static_cast<uint32_t>(ldr) * ES, ldt_b = static_cast<uint32_t>(ldt) * ES;
+    // the four results of register group (a, b, g): rows ib..ib+3 of column j
+    auto values = [&](int a, int b, int g, int ib, int j, const v4_t& e, float (&v)[4]) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      v4_t e[NB][4];
-      if (MODE == GM_POLY) {
+      for (int t = 0; t < 4; ++t) {
+        v[t] = acc[a][b][4 * g + t];
+        if (MODE == GM_POLY) {
+          v[t] = cb * to_f32(e[t]) + cc * v[t];
+          if (diag && ib + t == j && j < d.m) v[t] += ca;
+        }
+      }
+    };
+    auto load_e = [&](int ib, int j) {
+      return *at<const v4_t>(Ain, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(ib) * ES);
+    };
+    if (diag) {
+      // diagonal tile: the upper triangle only, with its mirror, so the two halves
+      // hold the same rounded values
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
             const int j = j0 + wn + b * 32 + l32;
-            e[b][g] = *reinterpret_cast<const v4_t*>(Ain + static_cast<int64_t>(j) * ldt + ib);
-          }
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-          const int j = j0 + wn + b * 32 + l32;
-          float v[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v[t] = acc[a][b][4 * g + t];
-            if (MODE == GM_POLY) {
-              v[t] = cb * to_f32(e[b][g][t]) + cc * v[t];
-              if (diag && ib + t == j && j < d.m) v[t] += ca;
-            }
-          }
-          if (!diag) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) C[static_cast<int64_t>(ib + t) * ldt + j] = from_f32<T>(v[t]);
-            store4<T>(C + static_cast<int64_t>(j) * ldt + ib, v[0], v[1], v[2], v[3]);
-          } else {
+            v4_t e = {};
+            if (MODE == GM_POLY) e = load_e(ib, j);
+            float v[4];
+            values(a, b, g, ib, j, e, v);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i = ib + t;
               if (i <= j) {
                 const T x = from_f32<T>(v[t]);
-                C[static_cast<int64_t>(i) * ldt + j] = x;
-                C[static_cast<int64_t>(j) * ldt + i] = x;
+                *at<T>(Cr, static_cast<uint32_t>(i) * ldt_b + static_cast<uint32_t>(j) * ES) = x;
+                *at<T>(Cr, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(i) * ES) = x;
               }
             }
           }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      unsigned char* stg = staging + wave * 4096;
+#pragma unroll
+      for (int p = 0; p < 4 / AP; ++p)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int j = j0 + wn + b * 32 + l32;
+          v4_t e[AP][4];
+          if (MODE == GM_POLY) {
+#pragma unroll
+            for (int ap = 0; ap < AP; ++ap)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) e[ap][g] = load_e(i0 + wm + (AP * p + ap) * 32 + 8 * g + 4 * half, j);
+          }
+#pragma unroll
+          for (int ap = 0; ap < AP; ++ap)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int a = AP * p + ap;
+              const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+              float v[4];
+              values(a, b, g, ib, j, e[ap][g], v);
+              const uint32_t o = static_cast<uint32_t>(ib) * ldr_b + static_cast<uint32_t>(j) * ES;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ldr_b) = from_f32<T>(v[t]);
+              const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+              const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the line
+              *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
+            }
+          // the wave's own LDS accesses execute in order: these reads see the writes
+          // above, and the next round's writes come after them
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jr = (lane >> 3) + 8 * r, c = lane & 7;
+            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
+            const uint32_t row = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
+            const uint32_t col = static_cast<uint32_t>(i0 + wm + 32 * AP * p) * ES + c * 16;
+            *at<u32x4_t>(Ct, row * ldt_b + col) = w;
+          }
+          __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
         }
     }
   } else {
-    T* X = static_cast<T*>(d.X);
-    T* XTn = static_cast<T*>(d.XT[parity ^ 1]);
-    const int64_t ldx = d.ldx;
-    TO* out = static_cast<TO*>(d.out);
+    const gptr<TO> out = global(static_cast<TO*>(d.out));
     const int m = d.m, n = d.n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -405,11 +598,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
           float v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
-          if (MODE == GM_APPLY) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) X[static_cast<int64_t>(ib + t) * ldx + j] = from_f32<T>(v[t]);
-            store4<T>(XTn + static_cast<int64_t>(j) * ldt + ib, v[0], v[1], v[2], v[3]);
-          } else if (j < n) {
+          if (j < n) {
             if (!d.transposed) {
               // out is m x n row-major
 #pragma unroll
@@ -417,7 +606,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
                 if (ib + t < m) out[static_cast<int64_t>(ib + t) * n + j] = from_f32<TO>(v[t]);
             } else {
               // out is n x m row-major: out[j][i]
-              TO* o = out + static_cast<int64_t>(j) * m + ib;
+              const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
               if (d.vec_ok && ib + 4 <= m) {
                 store4<TO>(o, v[0], v[1], v[2], v[3]);
               } else {
@@ -429,6 +618,13 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count,
           }
         }
     }
+    }
+    }
+    if (!has_next) break;
+    cur = nxt;
+    v += G;
+    has_next = v + G < total;
+    if (has_next) setup(v + G, nxt);
   }
 }
 

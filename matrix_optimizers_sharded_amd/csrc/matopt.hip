@@ -10,7 +10,8 @@
 //             A = X X^T,  B' = aI + bA + cA^2,  X <- B' X
 // Each launch covers every matrix of the batch (grouped launch); blocks find their
 // matrix by binary search over the table, which is sorted by decreasing size so
-// the longest tiles start first.
+// the longest tiles start first.  The GEMM launches are persistent: one block per
+// CU, each walking a strided share of the tile list.
 
 #include <hip/hip_runtime.h>
 
@@ -228,26 +229,42 @@ int launch(int pk, hipStream_t stream, F&& f) {
     if (rc_ != MO_OK) return rc_; \
   } while (0)
 
+// Blocks of a persistent GEMM launch: one per CU (the LDS ring admits no second
+// block), rounded down to a multiple of the 8 XCDs, never more than the work items.
+int64_t gemm_grid(int64_t total) {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int n = (dev >= 0 && dev < 64) ? cus[dev] : 0;
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 8;
+    if (dev >= 0 && dev < 64) cus[dev] = n;
+  }
+  const int64_t g = n >= 8 ? n / 8 * 8 : n;
+  return std::min<int64_t>(total, g);
+}
+
 template <typename T, typename TO>
 int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, hipStream_t stream) {
+  const int64_t gs = gemm_grid(plan.total[KIND_SYRK]), ga = gemm_grid(plan.total[KIND_APPLY]);
   for (int t = 0; t < ns.iters; ++t) {
     const int parity = t & 1;
     MO_TRY(launch(PK_SYRK, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(plan.total[KIND_SYRK]), dim3(NTHREADS), 0, stream,
-                         dd, count, parity, 0.f, 0.f, 0.f);
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
+                         dd, count, plan.total[KIND_SYRK], parity, 0.f, 0.f, 0.f);
     }));
     MO_TRY(launch(PK_POLY, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(plan.total[KIND_POLY]), dim3(NTHREADS), 0, stream,
-                         dd, count, parity, ns.a, ns.b, ns.c);
+      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
+                         dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c);
     }));
     const bool last = (t + 1 == ns.iters);
     MO_TRY(launch(PK_APPLY, stream, [&] {
       if (last)
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0,
-                           stream, dd, count, parity, 0.f, 0.f, 0.f);
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f);
       else
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(plan.total[KIND_APPLY]), dim3(NTHREADS), 0, stream,
-                           dd, count, parity, 0.f, 0.f, 0.f);
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f);
     }));
   }
   return MO_OK;
