@@ -388,6 +388,26 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // The waits count loads only: buffer loads complete in issue order, so "at most
   // n outstanding", with n the loads issued after slab kt+1's, means slab kt+1 is
   // in, whatever stores or atomics are also in flight.
+  // Within a k16 step the next step's fragment reads are interleaved one to one
+  // with this step's MFMAs (then the remaining MFMAs), so the LDS and the matrix
+  // cores work side by side instead of in turns.
+#ifndef MO_GEMM_INTERLEAVE
+#define MO_GEMM_INTERLEAVE 1
+#endif
+#if MO_GEMM_INTERLEAVE
+#define MO_STEP_FENCE() do {} while (0)
+#define MO_STEP_INTERLEAVE()                                                   \
+  do {                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4 + NB; ++i_) {                    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* one LDS read */    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */        \
+    }                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - 4 - NB, 0);           \
+  } while (0)
+#else
+#define MO_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define MO_STEP_INTERLEAVE() do {} while (0)
+#endif
   frag_t fa[2][4], fb[2][NB];
   auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
@@ -439,8 +459,9 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
 #pragma unroll
       for (int kk = 0; kk < KSTEPS - 1; ++kk) {
         read_frags(sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        MO_STEP_FENCE();
         mfma_step(fa[kk & 1], fb[kk & 1]);
+        MO_STEP_INTERLEAVE();
         __builtin_amdgcn_sched_barrier(0);
       }
       const int next = (stage + 1 == NSTAGE) ? 0 : stage + 1;
@@ -456,8 +477,9 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         if (own || has_next) issue(own ? cur : nxt, own ? ks : ks - cur.nk, stage);
       }
       read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
-      __builtin_amdgcn_sched_barrier(0);
+      MO_STEP_FENCE();
       mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
+      MO_STEP_INTERLEAVE();
       __builtin_amdgcn_sched_barrier(0);
       stage = next;
     }
