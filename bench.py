@@ -55,7 +55,9 @@ def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
 def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):
     """HBM roofline of the Sign-Muon kernels at a size where bandwidth, not launch
     latency, decides: sign_pack reads 4 B and writes 1/8 B per element (fp32 input);
-    sign_vote reads workers/8 B and writes 1/8 B per element."""
+    sign_vote reads workers/8 B and writes 1/8 B per element; sign_unpack reads 1/8 B
+    and writes 2 B (bf16 out); sign_apply reads 1/8 B and reads and writes 4 B (fp32
+    weight)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(12345)
     u = torch.randn(numel, generator=gen, device=dev, dtype=torch.float32)
@@ -66,22 +68,27 @@ def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):
         mo.sign_pack(u, packed[i])
     mo.sign_vote(packed, numel, out_packed=out)
     torch.cuda.synchronize()
+    signs = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    weight = torch.zeros(numel, dtype=torch.float32, device=dev)
+    mo.sign_unpack(out, numel, out=signs)
+    mo.sign_apply(out, weight, 1e-3)
+    torch.cuda.synchronize()
     mo.profile_begin()
     for _ in range(reps):
         mo.sign_pack(u, packed[0])
         mo.sign_vote(packed, numel, out_packed=out)
+        mo.sign_unpack(out, numel, out=signs)
+        mo.sign_apply(out, weight, 1e-3)
     torch.cuda.synchronize()
     k = mo.profile_end()
-    pack_ms = k["sign_pack"][1] / k["sign_pack"][0]
-    vote_ms = k["sign_vote"][1] / k["sign_vote"][0]
-    pack_b = numel * (4 + 1 / 8)
-    vote_b = numel * (workers + 1) / 8
-    res = {"numel": numel, "workers": workers,
-           "sign_pack": {"ms": round(pack_ms, 4), "gbs": round(pack_b / pack_ms / 1e6, 1),
-                         "frac_hbm": round(pack_b / pack_ms / 1e6 / PEAK_HBM_GBS, 4)},
-           "sign_vote": {"ms": round(vote_ms, 4), "gbs": round(vote_b / vote_ms / 1e6, 1),
-                         "frac_hbm": round(vote_b / vote_ms / 1e6 / PEAK_HBM_GBS, 4)}}
-    del u, packed, out
+    bytes_per = {"sign_pack": numel * (4 + 1 / 8), "sign_vote": numel * (workers + 1) / 8,
+                 "sign_unpack": numel * (1 / 8 + 2), "sign_apply": numel * (1 / 8 + 8)}
+    res = {"numel": numel, "workers": workers}
+    for name, nb in bytes_per.items():
+        t = k[name][1] / k[name][0]
+        res[name] = {"ms": round(t, 4), "gbs": round(nb / t / 1e6, 1),
+                     "frac_hbm": round(nb / t / 1e6 / PEAK_HBM_GBS, 4)}
+    del u, packed, out, signs, weight
     return res
 
 
@@ -143,6 +150,9 @@ def main():
     ap.add_argument("--sign-tail-numel", type=int, default=None,
                     help="also time sign_pack (fp32 input) and an 8-worker sign_vote on this many elements "
                          "(default: 2^28 for the sign-vote workload, off otherwise)")
+    ap.add_argument("--apply", action="store_true",
+                    help="time muon_step_apply (W <- W - lr*U fused into the last product, bf16 weights) "
+                         "instead of muon_step_batched")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -193,10 +203,19 @@ def main():
             grads.append(g)
             moms.append(m)
         out_dtype = torch.bfloat16 if compute == torch.bfloat16 else torch.float32
-        outs = [torch.empty(s, dtype=out_dtype, device=dev) for s in shapes]
+        if args.apply:
+            # weights: small values, updated in place every step
+            outs = [(torch.randn(s, device=dev) * 0.02).to(out_dtype) for s in shapes]
 
-        def step():
-            mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
+            def step():
+                mo.muon_step_apply(grads, moms, outs, BETA, *MUON_ABC, w.iters, 1e-3, EPS, compute=compute,
+                                   workspace=ws)
+        else:
+            outs = [torch.empty(s, dtype=out_dtype, device=dev) for s in shapes]
+
+            def step():
+                mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute,
+                                     workspace=ws)
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
@@ -285,7 +304,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "matrices": w.count, "params": numel, "ns_iters": w.iters,
                    "grad_dtype": w.grad_dtype, "momentum_dtype": "f32", "accumulate": "f32",
-                   "coefficients": list(MUON_ABC), "beta": BETA, "parallelism": "single GPU (owner-local)"},
+                   "coefficients": list(MUON_ABC), "beta": BETA, "parallelism": "single GPU (owner-local)",
+                   "step": "muon_step_apply (W -= lr*U fused)" if args.apply else "muon_step_batched"},
         "tflops": round(tflops, 2),
         "pct_peak": round(100.0 * tflops / peak, 2),
         "flops_per_step": f_alg,

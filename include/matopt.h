@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MATOPT_VERSION 100
+#define MATOPT_VERSION 110
 
 /* element types */
 enum { MO_F32 = 0, MO_BF16 = 1 };
@@ -95,8 +95,10 @@ size_t muon_workspace_bytes(const mo_matrix *mats, int32_t count, int32_t comput
  *   repeat ns->iters times: A = X X^T; B = b A + c A A; X <- a X + B X
  *   out <- X                   (caller's orientation, out_dtype)
  * grad_dtype: MO_F32 or MO_BF16.  compute_dtype: MO_F32 (fp32 operands) or MO_BF16
- * (bf16 operands X, A, B with fp32 accumulation; A and B are rounded to bf16 once
- * and b*A + c*A^2 is formed from the same rounded A).  out_dtype: MO_F32 or MO_BF16.
+ * (bf16 operands X, A, B with fp32 accumulation; A is rounded to bf16 once, and the
+ * polynomial matrix a*I + b*A + c*A^2 is formed from that same rounded A and rounded
+ * to bf16 once, so that each step is the single product X <- (a*I + b*A + c*A^2) X).
+ * out_dtype: MO_F32 or MO_BF16.
  * out must not overlap grad or momentum.  Deterministic: identical inputs give
  * bit-identical outputs, and a matrix's result does not depend on the rest of
  * the batch. */
@@ -126,6 +128,47 @@ int32_t sign_pack(const void *u, int32_t dtype, int64_t numel, uint32_t *packed,
  * int8 values sum_i = 2*count_i - M (needs M <= 127).  1 <= M <= 65535. */
 int32_t sign_vote(const uint32_t *packed, int32_t M, int64_t numel, uint32_t *out_packed,
                   int8_t *out_sum, void *stream);
+
+/* The step with the weight update fused in: the same computation as
+ * muon_step_batched, but the last Newton-Schulz product (or, for iters == 0, the
+ * scaled copy) updates the caller's weight in place instead of writing U:
+ *   W <- W - lr * U
+ * formed in fp32 from the unrounded U and stored in weight_dtype (MO_F32 or
+ * MO_BF16).  mats[i].out is W, rows*cols of weight_dtype, read and written; it must
+ * not overlap grad or momentum.  lr is finite (any sign).  The update form follows
+ * "Riepilogo Tecnico: SignMuon", Flusso Algoritmico item 4 (W - eta * direction),
+ * with the raw polar factor U as the direction: the pages give Muon no other
+ * scaling.  ("Riassunto Tecnico: MatrixFSDP", Metodologia item 1: the owner runs
+ * the update locally.) */
+int32_t muon_step_apply(const mo_matrix *mats, int32_t count, int32_t grad_dtype, int32_t compute_dtype,
+                        int32_t weight_dtype, float beta, const mo_ns_params *ns, float lr, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Inverse of sign_pack, for the optional local polar step on the voted signs
+ * ("Riepilogo Tecnico: SignMuon", Flusso Algoritmico item 5): out[i] = +1 where bit
+ * i of packed is set, -1 elsewhere; then ns_orthogonalize(out).  packed:
+ * ceil(numel/32) words; out: numel values of dtype (MO_F32 or MO_BF16).  numel >= 1. */
+int32_t sign_unpack(const uint32_t *packed, int64_t numel, int32_t dtype, void *out, void *stream);
+
+/* The Sign-Muon parameter update ("Riepilogo Tecnico: SignMuon", Flusso
+ * Algoritmico item 4): W <- W - lr * S, S[i] = +1 where bit i of packed (the voted
+ * signs) is set, -1 elsewhere.  The difference is formed in fp32 and stored in
+ * dtype (MO_F32 or MO_BF16).  weight: numel values, updated in place; lr finite. */
+int32_t sign_apply(const uint32_t *packed, int64_t numel, int32_t dtype, void *weight, float lr,
+                   void *stream);
+
+/* Owner planner, host only ("Riassunto Tecnico: MatrixFSDP", Metodologia, the
+ * MatrixShard metadata and global planner item: owners are chosen to balance
+ * resident bytes and optimizer work).  Work of matrix i is its algorithmic
+ * Newton-Schulz flops, iters * (3 m^2 n + m^3) with m = min(rows, cols),
+ * n = max(rows, cols); its bytes are rows*cols*bytes_per_element.  Matrices are
+ * taken in decreasing order of work (ties: more bytes first, then lower index) and
+ * each goes to the rank with the least work so far (ties: fewest bytes, then
+ * lowest rank).  owner: count entries in [0, ranks).  rank_work, rank_bytes:
+ * NULL or ranks entries each, the per-rank totals.  count >= 0, ranks >= 1, iters
+ * >= 0, bytes_per_element finite and >= 0. */
+int32_t mo_plan_owners(const int64_t *rows, const int64_t *cols, int32_t count, int32_t ranks, int32_t iters,
+                       double bytes_per_element, int32_t *owner, double *rank_work, double *rank_bytes);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *mo_last_error(void);

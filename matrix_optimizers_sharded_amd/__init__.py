@@ -12,9 +12,13 @@ from .binding import (  # noqa: F401
     load_library,
     library_path,
     muon_step_batched,
+    muon_step_apply,
     ns_orthogonalize,
     sign_pack,
     sign_vote,
+    sign_unpack,
+    sign_apply,
+    plan_owners,
     workspace_bytes,
     version,
     profile_begin,

@@ -63,6 +63,16 @@ def load_library():
     lib.sign_pack.restype = I32
     lib.sign_vote.argtypes = [P, I32, I64, P, P, P]
     lib.sign_vote.restype = I32
+    lib.muon_step_apply.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32, F,
+                                    ctypes.POINTER(MoNsParams), F, P, SZ, P]
+    lib.muon_step_apply.restype = I32
+    lib.sign_unpack.argtypes = [P, I64, I32, P, P]
+    lib.sign_unpack.restype = I32
+    lib.sign_apply.argtypes = [P, I64, I32, P, F, P]
+    lib.sign_apply.restype = I32
+    D = ctypes.c_double
+    lib.mo_plan_owners.argtypes = [P, P, I32, I32, I32, D, P, P, P]
+    lib.mo_plan_owners.restype = I32
     lib.mo_last_error.argtypes = []
     lib.mo_last_error.restype = ctypes.c_char_p
     lib.mo_version.argtypes = []
@@ -183,6 +193,35 @@ def muon_step_batched(grads, moms, outs, beta, a, b, c, iters, eps=1e-7, compute
                                  _stream_ptr(grads[0])))
 
 
+def muon_step_apply(grads, moms, weights, beta, a, b, c, iters, lr, eps=1e-7, compute=None,
+                    workspace=None):
+    """In place: moms[i] <- beta*moms[i] + grads[i]; weights[i] <- weights[i] - lr * U_i
+    with U_i = NS_k(moms[i] / (||.||+eps)), never materialised.  weights: fp32 or
+    bf16 (one dtype), shaped like the grads."""
+    import torch
+    lib = load_library()
+    if compute is None:
+        compute = torch.bfloat16
+    shapes = [tuple(g.shape) for g in grads]
+    if not (len(grads) == len(moms) == len(weights)):
+        raise MatoptError(-1, "grads, moms and weights must have the same length")
+    if not shapes:
+        return
+    _validate(grads, shapes, "grads", (torch.float32, torch.bfloat16))
+    _validate(moms, shapes, "moms", (torch.float32,))
+    _validate(weights, shapes, "weights", (torch.float32, torch.bfloat16))
+    gdt, wdt = grads[0].dtype, weights[0].dtype
+    if any(g.dtype != gdt for g in grads) or any(w.dtype != wdt for w in weights):
+        raise MatoptError(-2, "all grads (and all weights) must share one dtype")
+    mats = _mats(shapes, grads=grads, moms=moms, outs=weights)
+    nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
+    ws = (workspace or Workspace(grads[0].device)).get(nbytes)
+    ns = _ns_params(a, b, c, iters, eps)
+    _check(lib.muon_step_apply(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute), _dtype_code(wdt),
+                               float(beta), ctypes.byref(ns), float(lr), ws.data_ptr(), ws.numel(),
+                               _stream_ptr(grads[0])))
+
+
 def ns_orthogonalize(xs, outs, a, b, c, iters, eps=1e-7, compute=None, workspace=None):
     """outs[i] <- NS_k(xs[i] / (||xs[i]||_F + eps)); xs[i] may be outs[i] when the
     dtypes match."""
@@ -241,6 +280,55 @@ def sign_vote(packed, numel, out_packed=None, with_sums=False):
     _check(lib.sign_vote(packed.data_ptr(), M, numel, out_packed.data_ptr(),
                          sums.data_ptr() if sums is not None else None, _stream_ptr(packed)))
     return out_packed, sums
+
+
+def _check_packed(packed, numel):
+    import torch
+    if packed.dtype != torch.int32 or not packed.is_contiguous() or not packed.is_cuda:
+        raise MatoptError(-1, "packed must be a contiguous CUDA int32 tensor")
+    if packed.numel() < (numel + 31) // 32:
+        raise MatoptError(-1, "packed must hold ceil(numel/32) words")
+
+
+def sign_unpack(packed, numel, out=None, dtype=None):
+    """+1 / -1 per bit of packed (int32 words), as a flat tensor of numel values of
+    dtype (torch.bfloat16 by default) or into out."""
+    import torch
+    lib = load_library()
+    _check_packed(packed, numel)
+    if out is None:
+        out = torch.empty(numel, dtype=dtype or torch.bfloat16, device=packed.device)
+    if not out.is_cuda or not out.is_contiguous() or out.numel() != numel:
+        raise MatoptError(-1, "out must be a contiguous CUDA tensor of numel values")
+    _check(lib.sign_unpack(packed.data_ptr(), numel, _dtype_code(out.dtype), out.data_ptr(), _stream_ptr(packed)))
+    return out
+
+
+def sign_apply(packed, weight, lr):
+    """In place: weight <- weight - lr * S, S = +1 / -1 per bit of packed."""
+    lib = load_library()
+    numel = weight.numel()
+    _check_packed(packed, numel)
+    if not weight.is_cuda or not weight.is_contiguous():
+        raise MatoptError(-1, "weight must be a contiguous CUDA tensor")
+    _check(lib.sign_apply(packed.data_ptr(), numel, _dtype_code(weight.dtype), weight.data_ptr(), float(lr),
+                          _stream_ptr(weight)))
+    return weight
+
+
+def plan_owners(shapes, ranks, iters, bytes_per_element=4.0):
+    """Owner rank per matrix for a list of (rows, cols), plus per-rank work (NS flops)
+    and bytes.  Host-only computation in the library; needs no GPU."""
+    lib = load_library()
+    n = len(shapes)
+    I64s = ctypes.c_int64 * max(n, 1)
+    rows = I64s(*[int(r) for r, _ in shapes])
+    cols = I64s(*[int(c) for _, c in shapes])
+    owner = (ctypes.c_int32 * max(n, 1))()
+    work = (ctypes.c_double * max(int(ranks), 1))()
+    nbytes = (ctypes.c_double * max(int(ranks), 1))()
+    _check(lib.mo_plan_owners(rows, cols, n, int(ranks), int(iters), float(bytes_per_element), owner, work, nbytes))
+    return [owner[i] for i in range(n)], [work[r] for r in range(ranks)], [nbytes[r] for r in range(ranks)]
 
 
 def profile_begin():

@@ -150,11 +150,12 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
   }
 }
 
-// iters == 0: out = S * scale in the caller's orientation and out dtype.
+// iters == 0: out = S * scale in the caller's orientation and out dtype, or, when
+// applying to a weight, out <- out - lr * S * scale.
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void k_scaled_copy(const MatDesc* __restrict__ descs, int count,
                                                      const float* __restrict__ scale,
-                                                     int from_momentum) {
+                                                     int from_momentum, int apply, float lr) {
   const int64_t item = blockIdx.x;
   const MatDesc& d = descs[find_desc(descs, count, KIND_CHUNK, item)];
   const int64_t e0 = (item - d.begin[KIND_CHUNK]) * CHUNK;
@@ -163,8 +164,8 @@ __global__ __launch_bounds__(256) void k_scaled_copy(const MatDesc* __restrict__
   TO* out = static_cast<TO*>(d.out);
   const TS* sx = static_cast<const TS*>(d.grad);
   for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
-    const float v = from_momentum ? d.mom[e] : static_cast<float>(sx[e]);
-    out[e] = from_f32<TO>(v * s);
+    const float v = (from_momentum ? d.mom[e] : static_cast<float>(sx[e])) * s;
+    out[e] = from_f32<TO>(apply ? to_f32(out[e]) - lr * v : v);
   }
 }
 
@@ -254,6 +255,69 @@ __global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ 
         if (l < levels) c |= static_cast<int>((cnt[l] >> b) & 1u) << l;
       dst[b] = static_cast<int8_t>(2 * c - M);
     }
+  }
+}
+
+// The inverse of the packing, for the local polar step on the voted signs: element
+// i <- +1 where bit i is set, else -1.  One thread per 8 elements (one byte).
+template <typename T>
+__global__ __launch_bounds__(256) void k_sign_unpack(const uint32_t* __restrict__ packed, int64_t numel,
+                                                     T* __restrict__ out, int vec_ok) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e0 = t * 8;
+  if (e0 >= numel) return;
+  const uint32_t byte = (packed[t >> 2] >> (8 * (t & 3))) & 0xFFu;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = ((byte >> k) & 1u) ? 1.f : -1.f;
+  if (vec_ok && e0 + 8 <= numel) {
+    if (sizeof(T) == 4) {
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(out + e0);
+      p[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+      p[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+    } else {
+      bf16x8_t x;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = static_cast<bf16_t>(v[k]);
+      *reinterpret_cast<bf16x8_t*>(out + e0) = x;
+    }
+  } else {
+    for (int k = 0; k < 8 && e0 + k < numel; ++k) out[e0 + k] = from_f32<T>(v[k]);
+  }
+}
+
+// Sign-Muon parameter update W <- W - lr * S with S = +1 where bit i is set, else
+// -1: the difference is formed in fp32 and stored in W's dtype.  One thread per 8
+// elements.
+template <typename T>
+__global__ __launch_bounds__(256) void k_sign_apply(const uint32_t* __restrict__ packed, int64_t numel,
+                                                    T* __restrict__ w, float lr, int vec_ok) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e0 = t * 8;
+  if (e0 >= numel) return;
+  const uint32_t byte = (packed[t >> 2] >> (8 * (t & 3))) & 0xFFu;
+  if (vec_ok && e0 + 8 <= numel) {
+    if (sizeof(T) == 4) {
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(w + e0);
+      f32x4_t x0 = p[0], x1 = p[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x0[k] -= ((byte >> k) & 1u) ? lr : -lr;
+        x1[k] -= ((byte >> (k + 4)) & 1u) ? lr : -lr;
+      }
+      p[0] = x0;
+      p[1] = x1;
+    } else {
+      bf16x8_t* p = reinterpret_cast<bf16x8_t*>(w + e0);
+      bf16x8_t x = *p;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        x[k] = static_cast<bf16_t>(static_cast<float>(x[k]) - (((byte >> k) & 1u) ? lr : -lr));
+      *p = x;
+    }
+  } else {
+    for (int k = 0; k < 8 && e0 + k < numel; ++k)
+      w[e0 + k] = from_f32<T>(to_f32(w[e0 + k]) - (((byte >> k) & 1u) ? lr : -lr));
   }
 }
 

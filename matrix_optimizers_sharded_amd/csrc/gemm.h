@@ -32,7 +32,9 @@
 
 namespace mo {
 
-enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3 };
+// GM_APPLY_FINAL writes U to the caller's buffer; GM_APPLY_WEIGHT instead updates the
+// caller's weight in place, W <- W - lr * U, with lr passed as `ca`.
+enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3, GM_APPLY_WEIGHT = 4 };
 
 constexpr int GT = GEMM_TILE;          // 256
 
@@ -337,7 +339,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * pitch + lane_chunk;
     t.vPs = t.vQs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * pitch;
   };
-  static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND == 4, "loads per operand per wave: 2 or 4");
+  static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND % 4 == 0, "loads per operand per wave: 2 or 4k");
   auto issue = [&](const TileRef& t, int kt, int stage) {
     const uint32_t soff = kt * ROW_BYTES;
     const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
@@ -346,16 +348,19 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       const uint32_t v[4] = {t.vP0, t.vP0 + t.vPs, t.vQ0, t.vQ0 + t.vQs};
       load_lds16_2x2(t.rP, t.rQ, l, v, soff);
     } else {
-      uint32_t lp[4], lq[4], vp[4], vq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lp[q] = base + q * NWAVES * 1024;
-        lq[q] = lp[q] + OPERAND_BYTES;
-        vp[q] = t.vP0 + q * t.vPs;
-        vq[q] = t.vQ0 + q * t.vQs;
+      for (int q0 = 0; q0 < INST_PER_OPERAND; q0 += 4) {
+        uint32_t lp[4], lq[4], vp[4], vq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          lp[q] = base + (q0 + q) * NWAVES * 1024;
+          lq[q] = lp[q] + OPERAND_BYTES;
+          vp[q] = t.vP0 + (q0 + q) * t.vPs;
+          vq[q] = t.vQ0 + (q0 + q) * t.vQs;
+        }
+        load_lds16x4(t.rP, lp, vp, soff);
+        load_lds16x4(t.rQ, lq, vq, soff);
       }
-      load_lds16x4(t.rP, lp, vp, soff);
-      load_lds16x4(t.rQ, lq, vq, soff);
     }
   };
 
@@ -505,7 +510,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
   typedef typename Vec4<T>::type v4_t;
   const int64_t ldt = d.ldm;
-  if (MODE != GM_APPLY_FINAL) {
+  if (MODE != GM_APPLY_FINAL && MODE != GM_APPLY_WEIGHT) {
     constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128-byte line
     gptr<T> Cr, Ct;   // row-major and transposed destinations
     int64_t ldr;
@@ -620,21 +625,34 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           float v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
+          // the value stored at o: U itself, or W - lr * U
+          auto result = [&](gptr<TO> o, float u) {
+            return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);
+          };
           if (j < n) {
             if (!d.transposed) {
               // out is m x n row-major
 #pragma unroll
               for (int t = 0; t < 4; ++t)
-                if (ib + t < m) out[static_cast<int64_t>(ib + t) * n + j] = from_f32<TO>(v[t]);
+                if (ib + t < m) {
+                  const gptr<TO> o = out + static_cast<int64_t>(ib + t) * n + j;
+                  *o = result(o, v[t]);
+                }
             } else {
               // out is n x m row-major: out[j][i]
               const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
               if (d.vec_ok && ib + 4 <= m) {
+                if (MODE == GM_APPLY_WEIGHT) {
+                  typedef typename Vec4<TO>::type w4_t;
+                  const w4_t w = *reinterpret_cast<gptr<const w4_t>>(o);
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) v[t] = to_f32(w[t]) - ca * v[t];
+                }
                 store4<TO>(o, v[0], v[1], v[2], v[3]);
               } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                  if (ib + t < m) o[t] = from_f32<TO>(v[t]);
+                  if (ib + t < m) o[t] = result(o + t, v[t]);
               }
             }
           }

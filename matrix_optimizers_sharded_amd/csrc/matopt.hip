@@ -27,6 +27,7 @@
 #include "common.h"
 #include "elementwise.h"
 #include "gemm.h"
+#include "planner.h"
 
 using namespace mo;
 
@@ -190,8 +191,10 @@ bool g_prof = false;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_ev_pool;
 const char* const kKindNames[] = {"momentum_sumsq", "norm_scale", "prep_operand", "scaled_copy",
-                                  "ns_syrk", "ns_poly", "ns_apply", "sign_pack", "sign_vote"};
-enum { PK_MOM = 0, PK_SCALE, PK_PREP, PK_COPY, PK_SYRK, PK_POLY, PK_APPLY, PK_PACK, PK_VOTE, PK_N };
+                                  "ns_syrk",        "ns_poly",    "ns_apply",     "sign_pack",
+                                  "sign_vote",      "sign_unpack", "sign_apply"};
+enum { PK_MOM = 0, PK_SCALE, PK_PREP, PK_COPY, PK_SYRK, PK_POLY, PK_APPLY, PK_PACK, PK_VOTE, PK_UNPACK,
+       PK_SAPPLY, PK_N };
 
 hipEvent_t take_event() {
   if (!g_ev_pool.empty()) {
@@ -244,8 +247,16 @@ int64_t gemm_grid(int64_t total) {
   return std::min<int64_t>(total, g);
 }
 
+// Apply mode: the last APPLY (or the iters == 0 copy) updates the caller's weight,
+// out <- out - lr * U, instead of writing U.
+struct ApplyOpt {
+  bool on = false;
+  float lr = 0.f;
+};
+
 template <typename T, typename TO>
-int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, hipStream_t stream) {
+int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
+           hipStream_t stream) {
   const int64_t gs = gemm_grid(plan.total[KIND_SYRK]), ga = gemm_grid(plan.total[KIND_APPLY]);
   for (int t = 0; t < ns.iters; ++t) {
     const int parity = t & 1;
@@ -259,7 +270,10 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
     }));
     const bool last = (t + 1 == ns.iters);
     MO_TRY(launch(PK_APPLY, stream, [&] {
-      if (last)
+      if (last && ap.on)
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                           dd, count, plan.total[KIND_APPLY], parity, ap.lr, 0.f, 0.f);
+      else if (last)
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
                            dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f);
       else
@@ -272,35 +286,38 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
 
 template <typename TS, typename TC, typename TO>
 int run_after_scale(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
-                    const mo_ns_params& ns, hipStream_t stream) {
+                    const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
   const int from_mom = momentum ? 1 : 0;
   if (ns.iters == 0) {
     return launch(PK_COPY, stream, [&] {
       hipLaunchKernelGGL((k_scaled_copy<TS, TO>), dim3(plan.total[KIND_CHUNK]), dim3(256), 0, stream, dd,
-                         count, scale, from_mom);
+                         count, scale, from_mom, ap.on ? 1 : 0, ap.lr);
     });
   }
   MO_TRY(launch(PK_PREP, stream, [&] {
     hipLaunchKernelGGL((k_prep_operand<TS, TC>), dim3(plan.total[KIND_PREP]), dim3(256), 0, stream, dd,
                        count, scale, from_mom);
   }));
-  return run_ns<TC, TO>(dd, count, plan, ns, stream);
+  return run_ns<TC, TO>(dd, count, plan, ns, ap, stream);
 }
 
 template <typename TS>
 int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
-                         int compute, int out, const mo_ns_params& ns, hipStream_t stream) {
+                         int compute, int out, const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
   if (compute == MO_BF16) {
-    if (out == MO_BF16) return run_after_scale<TS, bf16_t, bf16_t>(dd, count, plan, scale, momentum, ns, stream);
-    return run_after_scale<TS, bf16_t, float>(dd, count, plan, scale, momentum, ns, stream);
+    if (out == MO_BF16)
+      return run_after_scale<TS, bf16_t, bf16_t>(dd, count, plan, scale, momentum, ns, ap, stream);
+    return run_after_scale<TS, bf16_t, float>(dd, count, plan, scale, momentum, ns, ap, stream);
   }
-  if (out == MO_BF16) return run_after_scale<TS, float, bf16_t>(dd, count, plan, scale, momentum, ns, stream);
-  return run_after_scale<TS, float, float>(dd, count, plan, scale, momentum, ns, stream);
+  if (out == MO_BF16) return run_after_scale<TS, float, bf16_t>(dd, count, plan, scale, momentum, ns, ap, stream);
+  return run_after_scale<TS, float, float>(dd, count, plan, scale, momentum, ns, ap, stream);
 }
 
 int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out, bool momentum, float beta,
-            const mo_ns_params* ns, void* workspace, size_t ws_bytes, void* stream_ptr) {
+            const mo_ns_params* ns, void* workspace, size_t ws_bytes, void* stream_ptr,
+            const ApplyOpt& ap = ApplyOpt()) {
   g_err.clear();
+  if (ap.on && !std::isfinite(ap.lr)) return fail(MO_ERR_INVALID, "lr must be finite");
   if (!ns) return fail(MO_ERR_INVALID, "ns params is NULL");
   if (!valid_dtype(in_dtype) || !valid_dtype(compute) || !valid_dtype(out))
     return fail(MO_ERR_UNSUPPORTED, "dtypes must be MO_F32 or MO_BF16");
@@ -344,8 +361,8 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   }));
   // after the momentum step the NS source is the fp32 momentum; otherwise the input
   if (momentum || in_dtype == MO_F32)
-    return dispatch_compute_out<float>(dd, count, full, scale, momentum, compute, out, *ns, stream);
-  return dispatch_compute_out<bf16_t>(dd, count, full, scale, momentum, compute, out, *ns, stream);
+    return dispatch_compute_out<float>(dd, count, full, scale, momentum, compute, out, *ns, ap, stream);
+  return dispatch_compute_out<bf16_t>(dd, count, full, scale, momentum, compute, out, *ns, ap, stream);
 }
 
 }  // namespace
@@ -364,6 +381,16 @@ int32_t muon_step_batched(const mo_matrix* mats, int32_t count, int32_t grad_dty
                           size_t workspace_bytes, void* stream) {
   return batched(mats, count, grad_dtype, compute_dtype, out_dtype, true, beta, ns, workspace, workspace_bytes,
                  stream);
+}
+
+int32_t muon_step_apply(const mo_matrix* mats, int32_t count, int32_t grad_dtype, int32_t compute_dtype,
+                        int32_t weight_dtype, float beta, const mo_ns_params* ns, float lr, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  ApplyOpt ap;
+  ap.on = true;
+  ap.lr = lr;
+  return batched(mats, count, grad_dtype, compute_dtype, weight_dtype, true, beta, ns, workspace, workspace_bytes,
+                 stream, ap);
 }
 
 int32_t ns_orthogonalize(const mo_matrix* mats, int32_t count, int32_t in_dtype, int32_t compute_dtype,
@@ -410,6 +437,61 @@ int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* ou
     hipLaunchKernelGGL(k_sign_vote, dim3(blocks), dim3(256), 0, stream, packed, M, levels, numel, nwords,
                        out_packed, out_sum);
   });
+}
+
+int32_t sign_unpack(const uint32_t* packed, int64_t numel, int32_t dtype, void* out, void* stream_ptr) {
+  g_err.clear();
+  if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
+  if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
+  if (!packed || !out) return fail(MO_ERR_INVALID, "packed or out is NULL");
+  const int64_t blocks = ((numel + 7) / 8 + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int vec = aligned16(out) ? 1 : 0;
+  return launch(PK_UNPACK, stream, [&] {
+    if (dtype == MO_F32)
+      hipLaunchKernelGGL((k_sign_unpack<float>), dim3(blocks), dim3(256), 0, stream, packed, numel,
+                         static_cast<float*>(out), vec);
+    else
+      hipLaunchKernelGGL((k_sign_unpack<bf16_t>), dim3(blocks), dim3(256), 0, stream, packed, numel,
+                         static_cast<bf16_t*>(out), vec);
+  });
+}
+
+int32_t sign_apply(const uint32_t* packed, int64_t numel, int32_t dtype, void* weight, float lr,
+                   void* stream_ptr) {
+  g_err.clear();
+  if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
+  if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
+  if (!packed || !weight) return fail(MO_ERR_INVALID, "packed or weight is NULL");
+  if (!std::isfinite(lr)) return fail(MO_ERR_INVALID, "lr must be finite");
+  const int64_t blocks = ((numel + 7) / 8 + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int vec = aligned16(weight) ? 1 : 0;
+  return launch(PK_SAPPLY, stream, [&] {
+    if (dtype == MO_F32)
+      hipLaunchKernelGGL((k_sign_apply<float>), dim3(blocks), dim3(256), 0, stream, packed, numel,
+                         static_cast<float*>(weight), lr, vec);
+    else
+      hipLaunchKernelGGL((k_sign_apply<bf16_t>), dim3(blocks), dim3(256), 0, stream, packed, numel,
+                         static_cast<bf16_t*>(weight), lr, vec);
+  });
+}
+
+int32_t mo_plan_owners(const int64_t* rows, const int64_t* cols, int32_t count, int32_t ranks, int32_t iters,
+                       double bytes_per_element, int32_t* owner, double* rank_work, double* rank_bytes) {
+  g_err.clear();
+  if (count < 0 || ranks < 1) return fail(MO_ERR_INVALID, "count must be >= 0 and ranks >= 1");
+  if (iters < 0) return fail(MO_ERR_INVALID, "iters must be >= 0");
+  if (!std::isfinite(bytes_per_element) || bytes_per_element < 0.0)
+    return fail(MO_ERR_INVALID, "bytes_per_element must be finite and >= 0");
+  if (count > 0 && (!rows || !cols || !owner)) return fail(MO_ERR_INVALID, "rows, cols or owner is NULL");
+  for (int i = 0; i < count; ++i)
+    if (rows[i] < 1 || cols[i] < 1 || rows[i] > MAX_DIM || cols[i] > MAX_DIM)
+      return fail(MO_ERR_INVALID, "matrix " + std::to_string(i) + ": rows and cols must be in [1, 2^24]");
+  plan_owners(rows, cols, count, ranks, iters, bytes_per_element, owner, rank_work, rank_bytes);
+  return MO_OK;
 }
 
 const char* mo_last_error(void) { return g_err.c_str(); }

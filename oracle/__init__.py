@@ -30,6 +30,7 @@ from .muon import (  # noqa: F401
     newton_schulz,
     ns_orthogonalize,
     muon_step,
+    weight_update,
     ns_polynomial_flops,
 )
 from .signs import (  # noqa: F401
@@ -38,4 +39,12 @@ from .signs import (  # noqa: F401
     unpack_bits,
     sign_pack,
     majority_vote,
+    unpack_signs,
+    sign_update,
+)
+from .planner import (  # noqa: F401
+    ns_work,
+    lpt_owners,
+    makespan,
+    optimal_makespan,
 )

@@ -126,6 +126,16 @@ def muon_step(grad, mom, beta, a, b, c, iters, eps, orient=True):
     return momentum_state_fp32(grad, mom, beta), u
 
 
+def weight_update(weight, u, lr):
+    """The owner's parameter update W - lr * U in float64.
+
+    The form follows "Riepilogo Tecnico: SignMuon", distributed flow item 4
+    (W_{t+1} = W_t - eta_t * direction), with the polar factor U itself as the Muon
+    direction: the pages give no other scaling for Muon (reading S7).  lr is taken
+    as the float32 value the caller passes."""
+    return np.asarray(weight, dtype=np.float64) - _f32_scalar(lr) * np.asarray(u, dtype=np.float64)
+
+
 def ns_polynomial_flops(rows, cols, iters):
     """Algorithmic flop count of the iteration on one r x s matrix: per step
     m^2 n (upper triangle of A = X X^T) + m^3 (A^2, symmetric) + 2 m^2 n (B X),

@@ -15,7 +15,12 @@ Readings of what the pages leave open:
     (least significant bit first), bit 1 means +1, unused bits of the last word are 0;
     M workers' packed buffers are stacked as a [M][nwords] array;
   * a tied vote (sum 0, possible for even M) resolves to +1;
-  * the integer sum is 2*count - M, which fits int8 for M <= 127.
+  * the integer sum is 2*count - M, which fits int8 for M <= 127;
+  * flow item 4 updates the weight with the voted signs, W <- W - eta * S; the
+    difference is formed in float32 and stored in the weight's dtype (float32, or
+    bfloat16 rounded to nearest even from that float32 value);
+  * flow item 5's optional local polar step takes the voted signs as +1 / -1
+    values.
 """
 
 import numpy as np
@@ -67,3 +72,41 @@ def majority_vote(packed, numel):
         counts += unpack_bits(packed[w], numel)
     sums = 2 * counts - M
     return pack_bits((sums >= 0).astype(np.uint8)), sums
+
+
+def unpack_signs(words, numel):
+    """The voted sign matrix as values: +1.0 where the bit is set, -1.0 elsewhere
+    (float64, flat order).  Input of the optional local polar step (flow item 5)."""
+    return np.where(unpack_bits(words, numel) == 1, 1.0, -1.0)
+
+
+def _round_bf16(x32):
+    """float32 -> nearest bfloat16 value, ties to the even one, returned as float64.
+
+    Written from the definition: the two bfloat16 neighbours of x are the values whose
+    low 16 bits of the float32 pattern are zero below and above x; pick the nearer,
+    on a tie the one whose last kept bit is 0.  Finite inputs only."""
+    x = np.asarray(x32, dtype=np.float32).reshape(-1)
+    bits = x.view(np.uint32).astype(np.uint64)
+    down = bits & np.uint64(0xFFFF0000)            # truncation towards zero
+    up = down + np.uint64(0x10000)                 # next value away from zero
+    lo = down.astype(np.uint32).view(np.float32).astype(np.float64)
+    hi = up.astype(np.uint32).view(np.float32).astype(np.float64)
+    xv = x.astype(np.float64)
+    d_lo, d_hi = np.abs(xv - lo), np.abs(hi - xv)
+    even_lo = ((down >> np.uint64(16)) & np.uint64(1)) == 0
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & even_lo)
+    return np.where(take_lo, lo, hi)
+
+
+def sign_update(weight, words, lr, bf16=False):
+    """W - lr * S for the voted signs S (flow item 4), as stored.
+
+    weight: float32 values (for bf16 weights, the float32 values of the bf16 numbers);
+    the difference is one float32 subtraction (numpy's float32 arithmetic is IEEE
+    correctly rounded), then rounded to bfloat16 when bf16=True.  Returns float64."""
+    w = np.asarray(weight, dtype=np.float32).reshape(-1)
+    s = unpack_signs(words, w.size).astype(np.float32)
+    step = np.float32(lr) * s                      # exact: multiplying by +-1
+    diff = (w - step).astype(np.float32)
+    return _round_bf16(diff) if bf16 else diff.astype(np.float64)

@@ -147,3 +147,12 @@ def test_muon_step_composes_momentum_and_ns():
     want_u = oracle.ns_orthogonalize(oracle.momentum_update(g, m, 0.95), *MUON_ABC, 5, EPS)
     np.testing.assert_array_equal(u, want_u)
     assert m_new.dtype == np.float32
+
+
+def test_weight_update_is_w_minus_lr_u():
+    w = np.array([[1.0, -2.0], [0.5, 0.0]])
+    u = np.array([[0.5, 0.25], [-1.0, 2.0]])
+    np.testing.assert_array_equal(oracle.weight_update(w, u, 0.5), [[0.75, -2.125], [1.0, -1.0]])
+    # lr passes through float32 at the C boundary: 0.1f, not 0.1
+    got = oracle.weight_update(np.zeros((1, 1)), np.ones((1, 1)), 0.1)
+    assert got[0, 0] == -float(np.float32(0.1)) != -0.1

@@ -79,3 +79,41 @@ def test_vote_invariants():
     pn = np.stack([oracle.pack_bits(1 - oracle.unpack_bits(r, numel)) for r in p])
     c, _ = oracle.majority_vote(pn, numel)
     np.testing.assert_array_equal(oracle.unpack_bits(c, numel), 1 - oracle.unpack_bits(a, numel))
+
+
+# ------------------------------------------------ voted-sign unpack and update
+
+@pytest.mark.parametrize("numel", [1, 5, 31, 32, 33, 95, 200])
+def test_unpack_signs_brute_force(numel):
+    rng = np.random.default_rng(numel)
+    words = rng.integers(0, 2 ** 32, (numel + 31) // 32, dtype=np.uint64).astype(np.uint32)
+    want = []
+    for i in range(numel):
+        bit = (int(words[i // 32]) >> (i % 32)) & 1
+        want.append(1.0 if bit else -1.0)
+    np.testing.assert_array_equal(oracle.unpack_signs(words, numel), np.array(want))
+
+
+def test_round_bf16_matches_torch_cpu_conversion():
+    import torch
+    from oracle.signs import _round_bf16
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.uniform(-6, 6, 20000)).astype(np.float32)
+    ties = (np.arange(1, 300, dtype=np.uint32) << 16 | 0x8000).view(np.float32)   # exact halfway points
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0, -1.5])])
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(_round_bf16(x), want)
+
+
+def test_sign_update_hand_cases():
+    words = np.array([0b0101], dtype=np.uint32)            # signs +1, -1, +1, -1
+    w = np.float32([1.0, 1.0, -2.0, 0.25])
+    got = oracle.sign_update(w, words, 0.5)
+    np.testing.assert_array_equal(got, [0.5, 1.5, -2.5, 0.75])
+    # bf16: 1 - 2^-9 lies exactly halfway between the bf16 numbers 1 - 2^-8 and 1;
+    # the even one is 1.0 (mantissa ...0)
+    got = oracle.sign_update(np.float32([1.0]), np.array([1], np.uint32), 2.0 ** -9, bf16=True)
+    np.testing.assert_array_equal(got, [1.0])
+    # float32 rounding: 1 + 2^-30 is not a float32 and rounds back to 1
+    got = oracle.sign_update(np.float32([1.0]), np.array([0], np.uint32), 2.0 ** -30)
+    np.testing.assert_array_equal(got, [1.0])
