@@ -208,53 +208,104 @@ __global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int6
   if ((lane & 3) == 0 && (t >> 2) < nwords) packed[t >> 2] = w;
 }
 
-// One thread per packed word: a bit-sliced counter adds the M workers' words (all
-// 32 bit positions at once), a bit-sliced compare gives count >= ceil(M/2), which
-// is 2*count - M >= 0 (ties -> +1).  Optionally the int8 sums 2*count - M.
-__global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M,
-                                                   int levels, int64_t numel, int64_t nwords,
-                                                   uint32_t* __restrict__ out,
-                                                   int8_t* __restrict__ out_sum) {
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (w >= nwords) return;
-  uint32_t cnt[16];
+// Vote of one group of W (1 or 4) consecutive words: a bit-sliced counter adds the
+// M workers' words (all 32 bit positions of every word at once), a bit-sliced
+// compare gives count >= ceil(M/2), which is 2*count - M >= 0 (ties -> +1).
+// Loads are issued 8 workers at a time ahead of the additions.  V is uint32_t or a
+// 4-vector of them; the counter has `levels` bit planes.
+template <typename V>
+__device__ inline V vote_group(const V* __restrict__ src, int64_t stride, int M, int levels, V (&cnt)[16]) {
 #pragma unroll
-  for (int l = 0; l < 16; ++l) cnt[l] = 0u;
-  for (int k = 0; k < M; ++k) {
-    uint32_t carry = packed[static_cast<int64_t>(k) * nwords + w];
+  for (int l = 0; l < 16; ++l) cnt[l] = V{} ^ V{};
+  int k = 0;
+  for (; k + 8 <= M; k += 8) {
+    V x[8];
 #pragma unroll
-    for (int l = 0; l < 16; ++l) {
+    for (int u = 0; u < 8; ++u) x[u] = src[static_cast<int64_t>(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      V carry = x[u];
+#pragma unroll
+      for (int l = 0; l < 16; ++l)
+        if (l < levels) {
+          const V c = cnt[l];
+          cnt[l] = c ^ carry;
+          carry = c & carry;
+        }
+    }
+  }
+  for (; k < M; ++k) {
+    V carry = src[static_cast<int64_t>(k) * stride];
+#pragma unroll
+    for (int l = 0; l < 16; ++l)
       if (l < levels) {
-        const uint32_t c = cnt[l];
+        const V c = cnt[l];
         cnt[l] = c ^ carry;
         carry = c & carry;
       }
-    }
   }
   // count >= T with T = ceil(M/2) <=> carry out of count + (2^levels - T)
   const uint32_t addend = (1u << levels) - static_cast<uint32_t>((M + 1) >> 1);
-  uint32_t carry = 0u;
+  V carry = V{} ^ V{};
 #pragma unroll
-  for (int l = 0; l < 16; ++l) {
+  for (int l = 0; l < 16; ++l)
     if (l < levels) {
-      const uint32_t k = ((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u;
-      carry = (cnt[l] & k) | ((cnt[l] ^ k) & carry);
+      const V kbits = V{} ^ V{} ^ (((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u);
+      carry = (cnt[l] & kbits) | ((cnt[l] ^ kbits) & carry);
+    }
+  return carry;
+}
+
+// int8 sums 2*count - M of the n (<= 32) elements of one word from its bit planes.
+__device__ inline void vote_sums(const uint32_t (&planes)[16], int levels, int M, int n, int8_t* dst) {
+  for (int b = 0; b < n; ++b) {
+    int c = 0;
+#pragma unroll
+    for (int l = 0; l < 16; ++l)
+      if (l < levels) c |= static_cast<int>((planes[l] >> b) & 1u) << l;
+    dst[b] = static_cast<int8_t>(2 * c - M);
+  }
+}
+
+// One thread per 4 packed words (16-byte loads) when the buffers allow it, else one
+// per word.  Pad bits of the last word are cleared.
+__global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M,
+                                                   int levels, int64_t numel, int64_t nwords,
+                                                   uint32_t* __restrict__ out,
+                                                   int8_t* __restrict__ out_sum, int quad) {
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int width = quad ? 4 : 1;
+  const int64_t w0 = t * width;
+  if (w0 >= nwords) return;
+  uint32_t words[4], planes[4][16];
+  int nw = 1;
+  if (quad && w0 + 4 <= nwords) {
+    u32x4v cnt[16];
+    const u32x4v v = vote_group<u32x4v>(reinterpret_cast<const u32x4v*>(packed + w0), nwords / 4, M, levels, cnt);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      words[q] = v[q];
+#pragma unroll
+      for (int l = 0; l < 16; ++l) planes[q][l] = cnt[l][q];
+    }
+    nw = 4;
+  } else {
+    nw = static_cast<int>(nwords - w0 < width ? nwords - w0 : width);
+    for (int q = 0; q < nw; ++q) {
+      uint32_t cnt[16];
+      words[q] = vote_group<uint32_t>(packed + w0 + q, nwords, M, levels, cnt);
+#pragma unroll
+      for (int l = 0; l < 16; ++l) planes[q][l] = cnt[l];
     }
   }
-  uint32_t valid = 0xFFFFFFFFu;
-  const int64_t tail = numel - w * 32;
-  if (tail < 32) valid = (1u << tail) - 1u;
-  out[w] = carry & valid;
-  if (out_sum) {
-    const int n = tail < 32 ? static_cast<int>(tail) : 32;
-    int8_t* dst = out_sum + w * 32;
-    for (int b = 0; b < n; ++b) {
-      int c = 0;
-#pragma unroll
-      for (int l = 0; l < 16; ++l)
-        if (l < levels) c |= static_cast<int>((cnt[l] >> b) & 1u) << l;
-      dst[b] = static_cast<int8_t>(2 * c - M);
-    }
+  for (int q = 0; q < nw; ++q) {
+    const int64_t w = w0 + q;
+    uint32_t valid = 0xFFFFFFFFu;
+    const int64_t tail = numel - w * 32;
+    if (tail < 32) valid = (1u << tail) - 1u;
+    out[w] = words[q] & valid;
+    if (out_sum) vote_sums(planes[q], levels, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + w * 32);
   }
 }
 

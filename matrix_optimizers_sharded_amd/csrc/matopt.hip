@@ -428,14 +428,18 @@ int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* ou
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !out_packed) return fail(MO_ERR_INVALID, "packed or out_packed is NULL");
   const int64_t nwords = (numel + 31) / 32;
-  const int64_t blocks = (nwords + 255) / 256;
+  // four words per thread with 16-byte loads when every worker's row starts 16-byte
+  // aligned (nwords % 4 == 0 and an aligned base)
+  const int quad = (nwords % 4 == 0 && aligned16(packed)) ? 1 : 0;
+  const int64_t threads = quad ? nwords / 4 : nwords;
+  const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   int levels = 0;
   while ((1 << levels) <= M) ++levels;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   return launch(PK_VOTE, stream, [&] {
     hipLaunchKernelGGL(k_sign_vote, dim3(blocks), dim3(256), 0, stream, packed, M, levels, numel, nwords,
-                       out_packed, out_sum);
+                       out_packed, out_sum, quad);
   });
 }
 

@@ -87,6 +87,29 @@ def test_sign_vote_large_M_without_sums(gpu):
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), oracle.majority_vote(packed, numel)[0])
 
 
+@pytest.mark.parametrize("M", [5, 1000])
+def test_sign_vote_four_word_path(gpu, M):
+    """nwords a multiple of 4 on a 16-byte aligned buffer takes the 4-words-per-thread
+    path; the same words on a base shifted by one word take the one-word path."""
+    import torch
+    from matrix_optimizers_sharded_amd import sign_vote
+    numel = 1024 * 32 - 3
+    nwords = 1024
+    rng = np.random.default_rng(M)
+    packed = rng.integers(0, 2 ** 32, size=(M, nwords), dtype=np.uint64).astype(np.uint32)
+    packed[:, -1] &= np.uint32((1 << (numel % 32)) - 1)
+    want = oracle.majority_vote(packed, numel)[0]
+    dev = torch.from_numpy(packed.view(np.int32)).to(gpu)
+    out, _ = sign_vote(dev, numel)
+    flat = torch.zeros(M * nwords + 1, dtype=torch.int32, device=gpu)
+    shifted = flat[1:].view(M, nwords)
+    shifted.copy_(dev)
+    out2, _ = sign_vote(shifted, numel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want)
+    np.testing.assert_array_equal(out2.cpu().numpy().view(np.uint32), want)
+
+
 # ---------------------------------------------------------------- Muon step
 
 def check_muon(grads, moms, got_m, got_u, compute, abc, iters, beta=BETA, eps=EPS, label=""):
