@@ -25,13 +25,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KINDS = [
     (re.compile(r"k_ns_gemm.*Li0E"), "ns_syrk"),
     (re.compile(r"k_ns_gemm.*Li1E"), "ns_poly"),
-    (re.compile(r"k_ns_gemm.*Li[23]E"), "ns_apply"),
+    (re.compile(r"k_ns_gemm.*Li[234]E"), "ns_apply"),
     (re.compile(r"k_momentum_sumsq"), "momentum_sumsq"),
     (re.compile(r"k_prep_operand"), "prep_operand"),
     (re.compile(r"k_norm_scale"), "norm_scale"),
     (re.compile(r"k_scaled_copy"), "scaled_copy"),
     (re.compile(r"k_sign_pack"), "sign_pack"),
     (re.compile(r"k_sign_vote"), "sign_vote"),
+    (re.compile(r"k_sign_unpack"), "sign_unpack"),
+    (re.compile(r"k_sign_apply"), "sign_apply"),
     (re.compile(r"__amd_rocclr_copyBuffer"), "device_copy"),
 ]
 
