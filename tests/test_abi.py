@@ -105,3 +105,38 @@ def test_invalid_arguments_fail_before_launch(lib):
 def test_profile_without_launches_is_empty(lib):
     assert lib.mo_profile_begin() == 0
     assert lib.mo_profile_end(None, 0) == 0
+
+
+def test_size_limits_are_rejected_on_the_host(lib):
+    # every padded operand buffer must stay below 2 GiB (32-bit buffer offsets)
+    ok = lib.muon_workspace_bytes(mats((16384, 32768)), 1, binding.MO_BF16)
+    assert ok > 3 * 16384 * 32768 * 2
+    assert lib.muon_workspace_bytes(mats((32768, 32768)), 1, binding.MO_BF16) == 0
+    assert b"2 GiB" in lib.mo_last_error()
+    # fp32 compute doubles the element size: the same matrix that fits in bf16 does not
+    assert lib.muon_workspace_bytes(mats((16384, 32768)), 1, binding.MO_F32) == 0
+    assert lib.muon_workspace_bytes(mats((1 << 25, 1)), 1, binding.MO_BF16) == 0
+    assert b"[1, 2^24]" in lib.mo_last_error()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.sign_pack(fake, 1, 1 << 45, fake, None) == -1
+    assert b"too large" in lib.mo_last_error()
+    assert lib.sign_unpack(fake, 1 << 45, 1, fake, None) == -1
+    assert lib.sign_apply(fake, 1 << 45, 1, fake, ctypes.c_float(0.1), None) == -1
+
+
+def test_next_row_calls_validate_arguments(lib):
+    fake = ctypes.c_void_p(0x1000)
+    ns = MoNsParams(3.4445, -4.775, 2.0315, 5, 1e-7)
+    m = mats((4, 4))
+    m[0].grad, m[0].momentum, m[0].out = 0x1000, 0x2000, 0x3000
+    assert lib.muon_step_apply(m, 1, 1, 1, 1, 0.9, ctypes.byref(ns), ctypes.c_float(float("inf")), fake,
+                               1 << 20, None) == -1
+    assert b"lr" in lib.mo_last_error()
+    assert lib.muon_step_apply(m, 1, 1, 1, 5, 0.9, ctypes.byref(ns), ctypes.c_float(0.1), fake, 1 << 20,
+                               None) == -2
+    assert lib.muon_step_apply(m, 0, 1, 1, 1, 0.9, ctypes.byref(ns), ctypes.c_float(0.1), None, 0, None) == 0
+    assert lib.sign_unpack(fake, 0, 1, fake, None) == -1
+    assert lib.sign_unpack(fake, 10, 3, fake, None) == -2
+    assert lib.sign_unpack(None, 10, 1, fake, None) == -1
+    assert lib.sign_apply(fake, 10, 1, None, ctypes.c_float(0.1), None) == -1
+    assert lib.sign_apply(fake, 10, 1, fake, ctypes.c_float(float("nan")), None) == -1
