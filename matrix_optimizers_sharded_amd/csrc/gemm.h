@@ -47,6 +47,12 @@ constexpr int GT = GEMM_TILE;          // 256
 #ifndef MO_GEMM_STAGES
 #define MO_GEMM_STAGES 2
 #endif
+// The staged whole-line stores of the transposed copies are non-temporal (+0.5%):
+// they are read again only by the next launch, so they need not displace operand
+// panels in L2.
+#ifndef MO_GEMM_NT_LINES
+#define MO_GEMM_NT_LINES 1
+#endif
 constexpr int ROW_BYTES = MO_GEMM_SLAB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
 constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
@@ -606,7 +612,11 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
             const uint32_t row = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
             const uint32_t col = static_cast<uint32_t>(i0 + wm + 32 * AP * p) * ES + c * 16;
+#if MO_GEMM_NT_LINES
+            __builtin_nontemporal_store(w, at<u32x4_t>(Ct, row * ldt_b + col));
+#else
             *at<u32x4_t>(Ct, row * ldt_b + col) = w;
+#endif
           }
           __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
         }
