@@ -107,6 +107,23 @@ __global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ 
 // (np x mp) in the compute dtype, zero outside the m x n corner.  The source tile
 // is read along its contiguous dimension and both outputs are written along theirs,
 // through an LDS tile.
+// Eight consecutive values stored with 16-byte stores (the address is 16-byte
+// aligned: workspace rows are multiples of 128 bytes and b is a multiple of 8).
+template <typename T>
+__device__ inline void store8(gptr<T> p, const float (&v)[8]);
+template <>
+__device__ inline void store8<bf16_t>(gptr<bf16_t> p, const float (&v)[8]) {
+  bf16x8_t x;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = static_cast<bf16_t>(v[k]);
+  *reinterpret_cast<gptr<bf16x8_t>>(p) = x;
+}
+template <>
+__device__ inline void store8<float>(gptr<float> p, const float (&v)[8]) {
+  reinterpret_cast<gptr<f32x4_t>>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<gptr<f32x4_t>>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+}
+
 template <typename TS, typename TC>
 __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict__ descs, int count,
                                                       const float* __restrict__ scale,
@@ -119,34 +136,60 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
   const int i0 = static_cast<int>(local / tn) * PREP_TILE;   // rows of X
   const int j0 = static_cast<int>(local % tn) * PREP_TILE;   // cols of X
   const float s = scale[d.scale_slot];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int t = threadIdx.x;
   const int64_t ld = d.cols;
   // source rows/cols of this tile: X[i][j] = S[i][j] (not transposed) or S[j][i]
   const int r0 = d.transposed ? j0 : i0, c0 = d.transposed ? i0 : j0;
   const int64_t rlim = d.rows, clim = d.cols;
   const float* sm = d.mom;
   const TS* sx = static_cast<const TS*>(d.grad);
+  if (d.vec_ok && r0 + PREP_TILE <= rlim && c0 + PREP_TILE <= clim) {
+    // whole tile inside the source: four consecutive elements per thread and load
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = (t >> 4) + 16 * q, b = (t & 15) * 4;
+      const int64_t e = (r0 + a) * ld + c0 + b;
+      float v[4];
+      if (from_momentum) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(sm + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = x[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = static_cast<float>(sx[e + k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tile[a][b + k] = v[k] * s;
+    }
+  } else {
+    const int tx = t & 63, ty = t >> 6;
 #pragma unroll 4
-  for (int q = 0; q < 16; ++q) {
-    const int a = ty + 4 * q;
-    const int64_t r = r0 + a, c = c0 + tx;
-    float v = 0.f;
-    if (r < rlim && c < clim) v = from_momentum ? sm[r * ld + c] : static_cast<float>(sx[r * ld + c]);
-    tile[a][tx] = v * s;
+    for (int q = 0; q < 16; ++q) {
+      const int a = ty + 4 * q;
+      const int64_t r = r0 + a, c = c0 + tx;
+      float v = 0.f;
+      if (r < rlim && c < clim) v = from_momentum ? sm[r * ld + c] : static_cast<float>(sx[r * ld + c]);
+      tile[a][tx] = v * s;
+    }
   }
   __syncthreads();
-  TC* X = static_cast<TC*>(d.X);
-  TC* XT = static_cast<TC*>(d.XT[0]);
+  // eight consecutive outputs per thread and store: a row of X (X[i0 + a][j0 + b ..])
+  // and a row of X^T (X^T[j0 + a][i0 + b ..] = X[i0 + b ..][j0 + a]); the padded
+  // tile (+1 column) keeps the column reads free of bank conflicts
+  const gptr<TC> X = global(static_cast<TC*>(d.X));
+  const gptr<TC> XT = global(static_cast<TC*>(d.XT[0]));
   const int64_t ldx = d.ldx, ldt = d.ldm;
-#pragma unroll 4
-  for (int q = 0; q < 16; ++q) {
-    const int a = ty + 4 * q;
-    // X[i0 + a][j0 + tx]
-    const float vx = d.transposed ? tile[tx][a] : tile[a][tx];
-    X[static_cast<int64_t>(i0 + a) * ldx + j0 + tx] = from_f32<TC>(vx);
-    // XT[j0 + a][i0 + tx] = X[i0 + tx][j0 + a]
-    const float vt = d.transposed ? tile[a][tx] : tile[tx][a];
-    XT[static_cast<int64_t>(j0 + a) * ldt + i0 + tx] = from_f32<TC>(vt);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int a = (t >> 3) + 32 * q, b = (t & 7) * 8;
+    float vx[8], vt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];
+      vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];
+    }
+    store8<TC>(X + static_cast<int64_t>(i0 + a) * ldx + j0 + b, vx);
+    store8<TC>(XT + static_cast<int64_t>(j0 + a) * ldt + i0 + b, vt);
   }
 }
 
