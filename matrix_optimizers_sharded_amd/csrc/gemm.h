@@ -73,9 +73,10 @@ constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / NWAVES;  // per wave, pe
 constexpr int INST_PER_SLAB = 2 * INST_PER_OPERAND;
 static_assert(GEMM_LDS_BYTES + NWAVES * 4096 <= 160 * 1024, "LDS ring and staging exceed 160 KiB");
 // the shortest K is 256: a tile has at least 512 / ROW_BYTES slabs (bf16), and the
-// persistent ring needs NSTAGE + 2 of them per tile
-static_assert(512 / ROW_BYTES >= NSTAGE + 2, "ring too deep for K = 256");
-static_assert(INST_PER_SLAB * (NSTAGE - 1) < 64, "vmcnt is a 6-bit field");
+// ring, which starts the next tile's loads during this tile's last NSTAGE slabs,
+// needs at least NSTAGE of them
+static_assert(512 / ROW_BYTES >= NSTAGE, "ring too deep for K = 256");
+static_assert(INST_PER_SLAB * 3 < 64, "vmcnt is a 6-bit field");
 
 // raw-buffer resource word 3 for gfx9-family: 32-bit data format, no swizzle
 constexpr int RSRC_FLAGS = 0x00020000;
@@ -336,7 +337,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       K = d->mp;
     }
     t.di = di;
-    t.nk = K / (ROW_BYTES / static_cast<int>(sizeof(T)));   // >= NSTAGE + 2: K >= 256
+    t.nk = K / (ROW_BYTES / static_cast<int>(sizeof(T)));   // >= 512 / ROW_BYTES >= NSTAGE: K >= 256
     const uint32_t pitch = static_cast<uint32_t>(ld) * esz;
     // X, A and B all have mp rows; X^T has np
     t.rP = buffer_rsrc(P, d->mp * pitch);
@@ -370,7 +371,6 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     }
   };
 
-
   f32x16_t acc[4][NB];
   auto zero_acc = [&]() {
 #pragma unroll
@@ -390,12 +390,12 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
 
   typedef typename Mfma<T>::frag frag_t;
   // Pipeline per slab kt (stage kt % NSTAGE), fragments double-buffered over the
-  // k16 steps: steps 0..KSTEPS-2 read the next step's fragments, then run 16 MFMAs;
+  // k16 steps: steps 0..KSTEPS-2 read the next step's fragments, then run 8 MFMAs;
   // then wait until this wave's loads of slab kt+1 have landed (later slabs may stay
   // in flight) and its own LDS reads are done, one barrier (slab kt+1 is in LDS for
   // everyone, and nobody reads slab kt any more), start the loads of slab
   // kt+NSTAGE (of this tile or the next) into slab kt's stage, read slab kt+1's
-  // first fragments; the last step's 16 MFMAs hide that barrier and those reads.
+  // first fragments; the last step's 8 MFMAs hide that barrier and those reads.
   // The waits count loads only: buffer loads complete in issue order, so "at most
   // n outstanding", with n the loads issued after slab kt+1's, means slab kt+1 is
   // in, whatever stores or atomics are also in flight.
@@ -438,12 +438,14 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   };
 
   static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth 2..5");
-  auto wait_loads = [&](int n) {   // at most n slabs' loads of this wave still in flight
-    if (NSTAGE > 4 && n >= 3)
+  // at most n slabs' loads of this wave still in flight (callers pass n <= NSTAGE - 1;
+  // more than 3 is waited for as 3)
+  auto wait_loads = [&](int n) {
+    if (n >= 3)
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * INST_PER_SLAB));
-    else if (NSTAGE > 3 && n >= 2)
+    else if (n == 2)
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * INST_PER_SLAB));
-    else if (NSTAGE > 2 && n >= 1)
+    else if (n == 1)
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(INST_PER_SLAB));
     else
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
@@ -496,179 +498,179 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     }
 
     {
-    // a uniform index, so the descriptor comes in through scalar loads, which no
-    // vmcnt wait covers (a vector load here would wait for the ring's loads too)
-    const MatDesc& d = descs[__builtin_amdgcn_readfirstlane(cur.di)];
-    const int ti = cur.ti, tj = cur.tj;
-    const int i0 = ti * GT, j0 = tj * GT;
-  // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
-  // ib..ib+3 of one column j per register group g.
-  //
-  // Row-major results (X', or C = A or B') are stored straight from the registers:
-  // one instruction writes 64 contiguous bytes of each of 8 rows.  The transposed
-  // copies (X'^T, the mirror tile of C) would leave the registers as 8 or 16 bytes
-  // per row per instruction, i.e. 8 partial writes per 128-byte line, and L2 write
-  // traffic of that shape slows everyone's operand loads.  They go through this
-  // wave's 4 KiB LDS staging slab instead: a round puts 32 columns j x 128 bytes of
-  // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
-  // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
-  // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
-  typedef typename Vec4<T>::type v4_t;
-  const int64_t ldt = d.ldm;
-  if (MODE != GM_APPLY_FINAL && MODE != GM_APPLY_WEIGHT) {
-    constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128-byte line
-    gptr<T> Cr, Ct;   // row-major and transposed destinations
-    int64_t ldr;
-    if (MODE == GM_APPLY) {
-      Cr = global(static_cast<T*>(d.X));
-      ldr = d.ldx;
-      Ct = global(static_cast<T*>(d.XT[parity ^ 1]));
-    } else {
-      Cr = Ct = global(static_cast<T*>(MODE == GM_SYRK ? d.A : d.B));
-      ldr = ldt;
-    }
-    const gptr<const T> Ain = global(static_cast<const T*>(d.A));
-    const bool diag = MODE != GM_APPLY && ti == tj;
-    // Every workspace buffer is below 2 GiB: element addresses are a uniform base
-    // plus a 32-bit byte offset, one VGPR per address.
-    constexpr uint32_t ES = sizeof(T);
-    const uint32_t ldr_b = static_cast<uint32_t>(ldr) * ES, ldt_b = static_cast<uint32_t>(ldt) * ES;
-    // the four results of register group (a, b, g): rows ib..ib+3 of column j
-    auto values = [&](int a, int b, int g, int ib, int j, const v4_t& e, float (&v)[4]) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[t] = acc[a][b][4 * g + t];
-        if (MODE == GM_POLY) {
-          v[t] = cb * to_f32(e[t]) + cc * v[t];
-          if (diag && ib + t == j && j < d.m) v[t] += ca;
+      // a uniform index, so the descriptor comes in through scalar loads, which no
+      // vmcnt wait covers (a vector load here would wait for the ring's loads too)
+      const MatDesc& d = descs[__builtin_amdgcn_readfirstlane(cur.di)];
+      const int ti = cur.ti, tj = cur.tj;
+      const int i0 = ti * GT, j0 = tj * GT;
+      // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
+      // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
+      // ib..ib+3 of one column j per register group g.
+      //
+      // Row-major results (X', or C = A or B') are stored straight from the registers:
+      // one instruction writes 64 contiguous bytes of each of 8 rows.  The transposed
+      // copies (X'^T, the mirror tile of C) would leave the registers as 8 or 16 bytes
+      // per row per instruction, i.e. 8 partial writes per 128-byte line, and L2 write
+      // traffic of that shape slows everyone's operand loads.  They go through this
+      // wave's 4 KiB LDS staging slab instead: a round puts 32 columns j x 128 bytes of
+      // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
+      // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
+      // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
+      typedef typename Vec4<T>::type v4_t;
+      const int64_t ldt = d.ldm;
+      if (MODE != GM_APPLY_FINAL && MODE != GM_APPLY_WEIGHT) {
+        constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128-byte line
+        gptr<T> Cr, Ct;   // row-major and transposed destinations
+        int64_t ldr;
+        if (MODE == GM_APPLY) {
+          Cr = global(static_cast<T*>(d.X));
+          ldr = d.ldx;
+          Ct = global(static_cast<T*>(d.XT[parity ^ 1]));
+        } else {
+          Cr = Ct = global(static_cast<T*>(MODE == GM_SYRK ? d.A : d.B));
+          ldr = ldt;
         }
-      }
-    };
-    auto load_e = [&](int ib, int j) {
-      return *at<const v4_t>(Ain, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(ib) * ES);
-    };
-    if (diag) {
-      // diagonal tile: the upper triangle only, with its mirror, so the two halves
-      // hold the same rounded values
+        const gptr<const T> Ain = global(static_cast<const T*>(d.A));
+        const bool diag = MODE != GM_APPLY && ti == tj;
+        // Every workspace buffer is below 2 GiB: element addresses are a uniform base
+        // plus a 32-bit byte offset, one VGPR per address.
+        constexpr uint32_t ES = sizeof(T);
+        const uint32_t ldr_b = static_cast<uint32_t>(ldr) * ES, ldt_b = static_cast<uint32_t>(ldt) * ES;
+        // the four results of register group (a, b, g): rows ib..ib+3 of column j
+        auto values = [&](int a, int b, int g, int ib, int j, const v4_t& e, float (&v)[4]) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-            const int j = j0 + wn + b * 32 + l32;
-            v4_t e = {};
-            if (MODE == GM_POLY) e = load_e(ib, j);
-            float v[4];
-            values(a, b, g, ib, j, e, v);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int i = ib + t;
-              if (i <= j) {
-                const T x = from_f32<T>(v[t]);
-                *at<T>(Cr, static_cast<uint32_t>(i) * ldt_b + static_cast<uint32_t>(j) * ES) = x;
-                *at<T>(Cr, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(i) * ES) = x;
-              }
+          for (int t = 0; t < 4; ++t) {
+            v[t] = acc[a][b][4 * g + t];
+            if (MODE == GM_POLY) {
+              v[t] = cb * to_f32(e[t]) + cc * v[t];
+              if (diag && ib + t == j && j < d.m) v[t] += ca;
             }
           }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      unsigned char* stg = staging + wave * 4096;
+        };
+        auto load_e = [&](int ib, int j) {
+          return *at<const v4_t>(Ain, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(ib) * ES);
+        };
+        if (diag) {
+          // diagonal tile: the upper triangle only, with its mirror, so the two halves
+          // hold the same rounded values
 #pragma unroll
-      for (int p = 0; p < 4 / AP; ++p)
+          for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int j = j0 + wn + b * 32 + l32;
-          v4_t e[AP][4];
-          if (MODE == GM_POLY) {
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int ap = 0; ap < AP; ++ap)
+              for (int g = 0; g < 4; ++g) {
+                const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+                const int j = j0 + wn + b * 32 + l32;
+                v4_t e = {};
+                if (MODE == GM_POLY) e = load_e(ib, j);
+                float v[4];
+                values(a, b, g, ib, j, e, v);
 #pragma unroll
-              for (int g = 0; g < 4; ++g) e[ap][g] = load_e(i0 + wm + (AP * p + ap) * 32 + 8 * g + 4 * half, j);
+                for (int t = 0; t < 4; ++t) {
+                  const int i = ib + t;
+                  if (i <= j) {
+                    const T x = from_f32<T>(v[t]);
+                    *at<T>(Cr, static_cast<uint32_t>(i) * ldt_b + static_cast<uint32_t>(j) * ES) = x;
+                    *at<T>(Cr, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(i) * ES) = x;
+                  }
+                }
+              }
+            __builtin_amdgcn_sched_barrier(0);
           }
+        } else {
+          unsigned char* stg = staging + wave * 4096;
 #pragma unroll
-          for (int ap = 0; ap < AP; ++ap)
+          for (int p = 0; p < 4 / AP; ++p)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const int j = j0 + wn + b * 32 + l32;
+              v4_t e[AP][4];
+              if (MODE == GM_POLY) {
+#pragma unroll
+                for (int ap = 0; ap < AP; ++ap)
+#pragma unroll
+                  for (int g = 0; g < 4; ++g) e[ap][g] = load_e(i0 + wm + (AP * p + ap) * 32 + 8 * g + 4 * half, j);
+              }
+#pragma unroll
+              for (int ap = 0; ap < AP; ++ap)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const int a = AP * p + ap;
+                  const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+                  float v[4];
+                  values(a, b, g, ib, j, e[ap][g], v);
+                  const uint32_t o = static_cast<uint32_t>(ib) * ldr_b + static_cast<uint32_t>(j) * ES;
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ldr_b) = from_f32<T>(v[t]);
+                  const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+                  const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the line
+                  *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
+                }
+              // the wave's own LDS accesses execute in order: these reads see the writes
+              // above, and the next round's writes come after them
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int jr = (lane >> 3) + 8 * r, c = lane & 7;
+                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
+                const uint32_t row = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
+                const uint32_t col = static_cast<uint32_t>(i0 + wm + 32 * AP * p) * ES + c * 16;
+#if MO_GEMM_NT_LINES
+                __builtin_nontemporal_store(w, at<u32x4_t>(Ct, row * ldt_b + col));
+#else
+                *at<u32x4_t>(Ct, row * ldt_b + col) = w;
+#endif
+              }
+              __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
+            }
+        }
+      } else {
+        const gptr<TO> out = global(static_cast<TO*>(d.out));
+        const int m = d.m, n = d.n;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int a = AP * p + ap;
               const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+              const int j = j0 + wn + b * 32 + l32;
               float v[4];
-              values(a, b, g, ib, j, e[ap][g], v);
-              const uint32_t o = static_cast<uint32_t>(ib) * ldr_b + static_cast<uint32_t>(j) * ES;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ldr_b) = from_f32<T>(v[t]);
-              const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-              const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the line
-              *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
-            }
-          // the wave's own LDS accesses execute in order: these reads see the writes
-          // above, and the next round's writes come after them
+              for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
+              // the value stored at o: U itself, or W - lr * U
+              auto result = [&](gptr<TO> o, float u) {
+                return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);
+              };
+              if (j < n) {
+                if (!d.transposed) {
+                  // out is m x n row-major
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jr = (lane >> 3) + 8 * r, c = lane & 7;
-            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
-            const uint32_t row = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
-            const uint32_t col = static_cast<uint32_t>(i0 + wm + 32 * AP * p) * ES + c * 16;
-#if MO_GEMM_NT_LINES
-            __builtin_nontemporal_store(w, at<u32x4_t>(Ct, row * ldt_b + col));
-#else
-            *at<u32x4_t>(Ct, row * ldt_b + col) = w;
-#endif
-          }
-          __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
-        }
-    }
-  } else {
-    const gptr<TO> out = global(static_cast<TO*>(d.out));
-    const int m = d.m, n = d.n;
+                  for (int t = 0; t < 4; ++t)
+                    if (ib + t < m) {
+                      const gptr<TO> o = out + static_cast<int64_t>(ib + t) * n + j;
+                      *o = result(o, v[t]);
+                    }
+                } else {
+                  // out is n x m row-major: out[j][i]
+                  const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
+                  if (d.vec_ok && ib + 4 <= m) {
+                    if (MODE == GM_APPLY_WEIGHT) {
+                      typedef typename Vec4<TO>::type w4_t;
+                      const w4_t w = *reinterpret_cast<gptr<const w4_t>>(o);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+                      for (int t = 0; t < 4; ++t) v[t] = to_f32(w[t]) - ca * v[t];
+                    }
+                    store4<TO>(o, v[0], v[1], v[2], v[3]);
+                  } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-          const int j = j0 + wn + b * 32 + l32;
-          float v[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
-          // the value stored at o: U itself, or W - lr * U
-          auto result = [&](gptr<TO> o, float u) {
-            return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);
-          };
-          if (j < n) {
-            if (!d.transposed) {
-              // out is m x n row-major
-#pragma unroll
-              for (int t = 0; t < 4; ++t)
-                if (ib + t < m) {
-                  const gptr<TO> o = out + static_cast<int64_t>(ib + t) * n + j;
-                  *o = result(o, v[t]);
+                    for (int t = 0; t < 4; ++t)
+                      if (ib + t < m) o[t] = result(o + t, v[t]);
+                  }
                 }
-            } else {
-              // out is n x m row-major: out[j][i]
-              const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
-              if (d.vec_ok && ib + 4 <= m) {
-                if (MODE == GM_APPLY_WEIGHT) {
-                  typedef typename Vec4<TO>::type w4_t;
-                  const w4_t w = *reinterpret_cast<gptr<const w4_t>>(o);
-#pragma unroll
-                  for (int t = 0; t < 4; ++t) v[t] = to_f32(w[t]) - ca * v[t];
-                }
-                store4<TO>(o, v[0], v[1], v[2], v[3]);
-              } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                  if (ib + t < m) o[t] = result(o + t, v[t]);
               }
             }
-          }
         }
-    }
-    }
+      }
     }
     if (!has_next) break;
     cur = nxt;
