@@ -175,10 +175,11 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
   __syncthreads();
   // eight consecutive outputs per thread and store: a row of X (X[i0 + a][j0 + b ..])
   // and a row of X^T (X^T[j0 + a][i0 + b ..] = X[i0 + b ..][j0 + a]); the padded
-  // tile (+1 column) keeps the column reads free of bank conflicts
-  const gptr<TC> X = global(static_cast<TC*>(d.X));
-  const gptr<TC> XT = global(static_cast<TC*>(d.XT[0]));
-  const int64_t ldx = d.ldx, ldt = d.ldm;
+  // tile (+1 column) keeps the column reads free of bank conflicts.  Both buffers are
+  // k-blocked along their columns, and eight consecutive columns from a multiple of
+  // 8 never straddle a k-block.
+  unsigned char* const X = static_cast<unsigned char*>(d.X);
+  unsigned char* const XT = static_cast<unsigned char*>(d.XT[0]);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int a = (t >> 3) + 32 * q, b = (t & 7) * 8;
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
       vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];
       vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];
     }
-    store8<TC>(X + static_cast<int64_t>(i0 + a) * ldx + j0 + b, vx);
-    store8<TC>(XT + static_cast<int64_t>(j0 + a) * ldt + i0 + b, vt);
+    store8<TC>(global(reinterpret_cast<TC*>(X + kb_off<TC>(i0 + a, j0 + b, d.pX))), vx);
+    store8<TC>(global(reinterpret_cast<TC*>(XT + kb_off<TC>(j0 + a, i0 + b, d.pT))), vt);
   }
 }
 

@@ -20,12 +20,13 @@
 // each owning a 128 x 64 sub-tile = 4 x 2 MFMA 32x32 blocks (128 fp32 accumulators
 // per lane), two waves per SIMD so that twice as many operand loads are in flight
 // as with 4 waves of 128 x 128 (the operand stream into LDS, not the MFMA rate, is
-// what bounds this kernel).  The k-loop streams 128-byte row slabs (64 bf16 or 32 fp32 of k) of both
-// operands straight from HBM/L2 into LDS with 16-byte buffer loads that write LDS
-// directly (no register staging), through a 2-stage ring: the loads of slab t+1
-// are in flight while slab t is multiplied.  LDS rows are 128 bytes with the 16-byte
-// chunk index XOR-swizzled by (r ^ r>>1) & 7, so the fragment reads of 8 or 16
-// consecutive rows hit distinct banks.
+// what bounds this kernel).  The k-loop streams slabs of 256 rows x 128 bytes (64
+// bf16 or 32 fp32 of k) of both operands, each one contiguous k-block of the
+// workspace layout, straight from HBM/L2 into LDS with 16-byte buffer loads that
+// write LDS directly (no register staging), through a 2-stage ring: the loads of
+// slab t+1 are in flight while slab t is multiplied.  LDS rows are 128 bytes with
+// the 16-byte chunk index XOR-swizzled by (r ^ r>>1) & 7, so the fragment reads of
+// 8 or 16 consecutive rows hit distinct banks.
 #pragma once
 
 #include "common.h"
@@ -38,14 +39,13 @@ enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3, GM_A
 
 constexpr int GT = GEMM_TILE;          // 256
 
-// k-slab geometry: each operand row of a slab is ROW_BYTES (128: 64 bf16 / 32 fp32 of
-// k), and NSTAGE slabs are in flight in an LDS ring, so the loads of slab t+NSTAGE-1
-// overlap the MFMAs of slabs t .. t+NSTAGE-2.
-#ifndef MO_GEMM_SLAB_BYTES
-#define MO_GEMM_SLAB_BYTES 128
-#endif
+// k-slab geometry: each operand row of a slab is ROW_BYTES, one k-block of the
+// workspace layout (128: 64 bf16 / 32 fp32 of k), and NSTAGE slabs are in flight in
+// an LDS ring, so the loads of slab t+NSTAGE-1 overlap the MFMAs of slabs t ..
+// t+NSTAGE-2.  (With 64-byte blocks the ring holds four 32 KiB stages, three slabs
+// of load cover instead of one; the extra barriers ate the gain.)
 #ifndef MO_GEMM_STAGES
-#define MO_GEMM_STAGES 2
+#define MO_GEMM_STAGES (MO_GEMM_SLAB_BYTES == 64 ? 4 : 2)
 #endif
 // The staged whole-line stores of the transposed copies are non-temporal (+0.5%):
 // they are read again only by the next launch, so they need not displace operand
@@ -53,7 +53,7 @@ constexpr int GT = GEMM_TILE;          // 256
 #ifndef MO_GEMM_NT_LINES
 #define MO_GEMM_NT_LINES 1
 #endif
-constexpr int ROW_BYTES = MO_GEMM_SLAB_BYTES;
+constexpr int ROW_BYTES = KB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
 constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
 constexpr int NSTAGE = MO_GEMM_STAGES;
@@ -132,9 +132,10 @@ __device__ inline void load_lds16x4(i32x4_t rsrc, const uint32_t (&lds)[4], cons
         "s"(so)
       : "memory");
 }
-// The same for two loads from each of two buffers (P then Q) in one block.
+// The same for two loads from each of two buffers (P then Q) in one block, with a
+// scalar offset per buffer.
 __device__ inline void load_lds16_2x2(i32x4_t rsrc_p, i32x4_t rsrc_q, const uint32_t (&lds)[4],
-                                      const uint32_t (&voff)[4], uint32_t soff) {
+                                      const uint32_t (&voff)[4], uint32_t soff_p, uint32_t soff_q) {
   i32x4_t rp, rq;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -143,18 +144,18 @@ __device__ inline void load_lds16_2x2(i32x4_t rsrc_p, i32x4_t rsrc_q, const uint
   }
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds[0]), l1 = __builtin_amdgcn_readfirstlane(lds[1]);
   const uint32_t l2 = __builtin_amdgcn_readfirstlane(lds[2]), l3 = __builtin_amdgcn_readfirstlane(lds[3]);
-  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t sp = __builtin_amdgcn_readfirstlane(soff_p), sq = __builtin_amdgcn_readfirstlane(soff_q);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %11 offen lds\n\t"
       "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %11 offen lds\n\t"
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %10, %11 offen lds\n\t"
-      "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %10, %11 offen lds\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %10, %12 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %10, %12 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rp),
-        "s"(rq), "s"(so)
+        "s"(rq), "s"(sp), "s"(sq)
       : "memory");
 }
 
@@ -272,7 +273,8 @@ __device__ inline void store4(gptr<T> p, float v0, float v1, float v2, float v3)
 struct TileRef {
   int di, ti, tj, nk;   // descriptor index, tile row and column, k slabs
   i32x4_t rP, rQ;
-  uint32_t vP0, vQ0, vPs, vQs;
+  uint32_t vP0, vQ0;    // this lane's byte offsets in k-block 0 of P and Q
+  uint32_t kP, kQ;      // k-block pitch (bytes) of P and Q: the step from slab to slab
 };
 
 // Persistent kernel: the grid holds at most one block per CU, and block b walks the
@@ -313,47 +315,45 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     const int64_t local = item - d->begin[kind];
     const T* P;
     const T* Q;
-    int64_t ld;
-    uint32_t rowsQ;
+    uint32_t kP, kQ;   // k-block pitches
     int K;
     if (MODE == GM_SYRK) {
       upper_tile(local, d->mp / GT, t.ti, t.tj);
       P = Q = static_cast<const T*>(d->X);
-      ld = d->ldx;
-      rowsQ = d->mp;
+      kP = kQ = d->pX;
       K = d->np;
     } else if (MODE == GM_POLY) {
       upper_tile(local, d->mp / GT, t.ti, t.tj);
       P = Q = static_cast<const T*>(d->A);
-      ld = d->ldm;
-      rowsQ = d->mp;
+      kP = kQ = d->pM;
       K = d->mp;
     } else {
       rect_tile(local, d->mp / GT, d->np / GT, t.ti, t.tj);
       P = static_cast<const T*>(d->B);
       Q = static_cast<const T*>(d->XT[parity]);
-      ld = d->ldm;
-      rowsQ = d->np;
+      kP = d->pM;
+      kQ = d->pT;
       K = d->mp;
     }
     t.di = di;
     t.nk = K / (ROW_BYTES / static_cast<int>(sizeof(T)));   // >= 512 / ROW_BYTES >= NSTAGE: K >= 256
-    const uint32_t pitch = static_cast<uint32_t>(ld) * esz;
-    // X, A and B all have mp rows; X^T has np
-    t.rP = buffer_rsrc(P, d->mp * pitch);
-    t.rQ = buffer_rsrc(Q, rowsQ * pitch);
-    t.vP0 = static_cast<uint32_t>(t.ti * GT + row0) * pitch + lane_chunk;
-    t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * pitch + lane_chunk;
-    t.vPs = t.vQs = static_cast<uint32_t>(ROWS_PER_INST * NWAVES) * pitch;
+    t.rP = buffer_rsrc(P, t.nk * kP);
+    t.rQ = buffer_rsrc(Q, t.nk * kQ);
+    t.vP0 = static_cast<uint32_t>(t.ti * GT + row0) * ROW_BYTES + lane_chunk;
+    t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * ROW_BYTES + lane_chunk;
+    t.kP = kP;
+    t.kQ = kQ;
   };
   static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND % 4 == 0, "loads per operand per wave: 2 or 4k");
+  // rows advance by ROWS_PER_INST * NWAVES from one of a wave's loads to the next
+  constexpr uint32_t VSTEP = ROWS_PER_INST * NWAVES * ROW_BYTES;
   auto issue = [&](const TileRef& t, int kt, int stage) {
-    const uint32_t soff = kt * ROW_BYTES;
+    const uint32_t sp = kt * t.kP, sq = kt * t.kQ;   // k-block kt of P and of Q
     const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
     if (INST_PER_OPERAND == 2) {
       const uint32_t l[4] = {base, base + NWAVES * 1024, base + OPERAND_BYTES, base + OPERAND_BYTES + NWAVES * 1024};
-      const uint32_t v[4] = {t.vP0, t.vP0 + t.vPs, t.vQ0, t.vQ0 + t.vQs};
-      load_lds16_2x2(t.rP, t.rQ, l, v, soff);
+      const uint32_t v[4] = {t.vP0, t.vP0 + VSTEP, t.vQ0, t.vQ0 + VSTEP};
+      load_lds16_2x2(t.rP, t.rQ, l, v, sp, sq);
     } else {
 #pragma unroll
       for (int q0 = 0; q0 < INST_PER_OPERAND; q0 += 4) {
@@ -362,11 +362,11 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         for (int q = 0; q < 4; ++q) {
           lp[q] = base + (q0 + q) * NWAVES * 1024;
           lq[q] = lp[q] + OPERAND_BYTES;
-          vp[q] = t.vP0 + (q0 + q) * t.vPs;
-          vq[q] = t.vQ0 + (q0 + q) * t.vQs;
+          vp[q] = t.vP0 + (q0 + q) * VSTEP;
+          vq[q] = t.vQ0 + (q0 + q) * VSTEP;
         }
-        load_lds16x4(t.rP, lp, vp, soff);
-        load_lds16x4(t.rQ, lq, vq, soff);
+        load_lds16x4(t.rP, lp, vp, sp);
+        load_lds16x4(t.rQ, lq, vq, sq);
       }
     }
   };
@@ -507,35 +507,37 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
       // ib..ib+3 of one column j per register group g.
       //
-      // Row-major results (X', or C = A or B') are stored straight from the registers:
-      // one instruction writes 64 contiguous bytes of each of 8 rows.  The transposed
-      // copies (X'^T, the mirror tile of C) would leave the registers as 8 or 16 bytes
-      // per row per instruction, i.e. 8 partial writes per 128-byte line, and L2 write
+      // Both destinations are k-blocked along their columns (a 128-byte k-block row is
+      // one line).  Row-major results (X', or C = A or B') are stored straight from the
+      // registers: one instruction writes 64 contiguous bytes of each of 2 rows.  The
+      // transposed copies (X'^T, the mirror tile of C) would leave the registers as 8
+      // or 16 bytes per row per instruction, i.e. 8 partial writes per line, and L2 write
       // traffic of that shape slows everyone's operand loads.  They go through this
       // wave's 4 KiB LDS staging slab instead: a round puts 32 columns j x 128 bytes of
       // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
       // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
       // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
       typedef typename Vec4<T>::type v4_t;
-      const int64_t ldt = d.ldm;
       if (MODE != GM_APPLY_FINAL && MODE != GM_APPLY_WEIGHT) {
-        constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128-byte line
-        gptr<T> Cr, Ct;   // row-major and transposed destinations
-        int64_t ldr;
+        constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128 bytes of k
+        // row-major and transposed destinations (C[i][j] and C^T[j][i], both k-blocked
+        // along their columns) and their k-block pitches
+        gptr<T> Cr, Ct;
+        uint32_t pr, pt;
         if (MODE == GM_APPLY) {
           Cr = global(static_cast<T*>(d.X));
-          ldr = d.ldx;
+          pr = d.pX;
           Ct = global(static_cast<T*>(d.XT[parity ^ 1]));
+          pt = d.pT;
         } else {
           Cr = Ct = global(static_cast<T*>(MODE == GM_SYRK ? d.A : d.B));
-          ldr = ldt;
+          pr = pt = d.pM;
         }
         const gptr<const T> Ain = global(static_cast<const T*>(d.A));
         const bool diag = MODE != GM_APPLY && ti == tj;
         // Every workspace buffer is below 2 GiB: element addresses are a uniform base
         // plus a 32-bit byte offset, one VGPR per address.
         constexpr uint32_t ES = sizeof(T);
-        const uint32_t ldr_b = static_cast<uint32_t>(ldr) * ES, ldt_b = static_cast<uint32_t>(ldt) * ES;
         // the four results of register group (a, b, g): rows ib..ib+3 of column j
         auto values = [&](int a, int b, int g, int ib, int j, const v4_t& e, float (&v)[4]) {
 #pragma unroll
@@ -547,9 +549,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             }
           }
         };
-        auto load_e = [&](int ib, int j) {
-          return *at<const v4_t>(Ain, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(ib) * ES);
-        };
+        // A[j][ib..ib+3]: four consecutive k of one row, inside one k-block
+        auto load_e = [&](int ib, int j) { return *at<const v4_t>(Ain, kb_off<T>(j, ib, d.pM)); };
         if (diag) {
           // diagonal tile: the upper triangle only, with its mirror, so the two halves
           // hold the same rounded values
@@ -570,8 +571,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                   const int i = ib + t;
                   if (i <= j) {
                     const T x = from_f32<T>(v[t]);
-                    *at<T>(Cr, static_cast<uint32_t>(i) * ldt_b + static_cast<uint32_t>(j) * ES) = x;
-                    *at<T>(Cr, static_cast<uint32_t>(j) * ldt_b + static_cast<uint32_t>(i) * ES) = x;
+                    *at<T>(Cr, kb_off<T>(i, j, pr)) = x;
+                    *at<T>(Cr, kb_off<T>(j, i, pr)) = x;
                   }
                 }
               }
@@ -599,11 +600,13 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                   const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
                   float v[4];
                   values(a, b, g, ib, j, e[ap][g], v);
-                  const uint32_t o = static_cast<uint32_t>(ib) * ldr_b + static_cast<uint32_t>(j) * ES;
+                  // rows ib..ib+3 of column j: consecutive rows of one k-block are
+                  // ROW_BYTES apart, and a half-wave writes 64 contiguous bytes per row
+                  const uint32_t o = kb_off<T>(ib, j, pr);
 #pragma unroll
-                  for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ldr_b) = from_f32<T>(v[t]);
+                  for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ROW_BYTES) = from_f32<T>(v[t]);
                   const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-                  const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the line
+                  const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the staged row
                   *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
                 }
               // the wave's own LDS accesses execute in order: these reads see the writes
@@ -612,12 +615,15 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
               for (int r = 0; r < 4; ++r) {
                 const int jr = (lane >> 3) + 8 * r, c = lane & 7;
                 const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
-                const uint32_t row = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
-                const uint32_t col = static_cast<uint32_t>(i0 + wm + 32 * AP * p) * ES + c * 16;
+                // 16 bytes of row j of C^T, from column i0 + wm + 32 AP p + c (16 / es)
+                // on; the 8 lanes of row j fill one whole k-block row (with 64-byte
+                // k-blocks, rows j and j + 1, j even, share the line)
+                const uint32_t jrow = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
+                const uint32_t icol = static_cast<uint32_t>(i0 + wm + 32 * AP * p) + c * (16 / sizeof(T));
 #if MO_GEMM_NT_LINES
-                __builtin_nontemporal_store(w, at<u32x4_t>(Ct, row * ldt_b + col));
+                __builtin_nontemporal_store(w, at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)));
 #else
-                *at<u32x4_t>(Ct, row * ldt_b + col) = w;
+                *at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)) = w;
 #endif
               }
               __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
