@@ -47,12 +47,21 @@ constexpr int GT = GEMM_TILE;          // 256
 #ifndef MO_GEMM_STAGES
 #define MO_GEMM_STAGES (MO_GEMM_SLAB_BYTES == 64 ? 4 : 2)
 #endif
-// The staged whole-line stores of the transposed copies are non-temporal (+0.5%):
-// they are read again only by the next launch, so they need not displace operand
-// panels in L2.
-#ifndef MO_GEMM_NT_LINES
-#define MO_GEMM_NT_LINES 1
+// The epilogue's stores into the workspace are non-temporal: they are read again
+// only by the next launch, so they need not displace the operand panels that the
+// other blocks of an XCD are sharing in L2.  Measured: -0.5% time for the staged
+// whole-line transposed copies, a further -1.1% for the row-major results.
+#ifndef MO_GEMM_NT_STORES
+#define MO_GEMM_NT_STORES 1
 #endif
+template <typename V>
+__device__ inline void store_ws(gptr<V> p, const V& v) {
+#if MO_GEMM_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 constexpr int ROW_BYTES = KB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
 constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
@@ -571,8 +580,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                   const int i = ib + t;
                   if (i <= j) {
                     const T x = from_f32<T>(v[t]);
-                    *at<T>(Cr, kb_off<T>(i, j, pr)) = x;
-                    *at<T>(Cr, kb_off<T>(j, i, pr)) = x;
+                    store_ws(at<T>(Cr, kb_off<T>(i, j, pr)), x);
+                    store_ws(at<T>(Cr, kb_off<T>(j, i, pr)), x);
                   }
                 }
               }
@@ -604,7 +613,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                   // ROW_BYTES apart, and a half-wave writes 64 contiguous bytes per row
                   const uint32_t o = kb_off<T>(ib, j, pr);
 #pragma unroll
-                  for (int t = 0; t < 4; ++t) *at<T>(Cr, o + t * ROW_BYTES) = from_f32<T>(v[t]);
+                  for (int t = 0; t < 4; ++t) store_ws(at<T>(Cr, o + t * ROW_BYTES), from_f32<T>(v[t]));
                   const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
                   const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the staged row
                   *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
@@ -620,11 +629,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                 // k-blocks, rows j and j + 1, j even, share the line)
                 const uint32_t jrow = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
                 const uint32_t icol = static_cast<uint32_t>(i0 + wm + 32 * AP * p) + c * (16 / sizeof(T));
-#if MO_GEMM_NT_LINES
-                __builtin_nontemporal_store(w, at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)));
-#else
-                *at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)) = w;
-#endif
+                store_ws(at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)), w);
               }
               __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
             }
