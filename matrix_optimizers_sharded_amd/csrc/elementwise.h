@@ -252,104 +252,95 @@ __global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int6
   if ((lane & 3) == 0 && (t >> 2) < nwords) packed[t >> 2] = w;
 }
 
-// Vote of one group of W (1 or 4) consecutive words: a bit-sliced counter adds the
-// M workers' words (all 32 bit positions of every word at once), a bit-sliced
-// compare gives count >= ceil(M/2), which is 2*count - M >= 0 (ties -> +1).
-// Loads are issued 8 workers at a time ahead of the additions.  V is uint32_t or a
-// 4-vector of them; the counter has `levels` bit planes.
-template <typename V>
-__device__ inline V vote_group(const V* __restrict__ src, int64_t stride, int M, int levels, V (&cnt)[16]) {
+__device__ inline uint32_t lane_word(uint32_t v, int) { return v; }
+__device__ inline uint32_t lane_word(const u32x4_t& v, int q) { return v[q]; }
+
+// Vote of one group of W (1 or 4) consecutive words: a bit-sliced counter of LV bit
+// planes (2^LV > M) adds the M workers' words (all 32 bit positions of every word at
+// once), and a bit-sliced compare gives count >= ceil(M/2), which is
+// 2*count - M >= 0 (ties -> +1).  Loads are issued 8 workers at a time ahead of the
+// additions.  V is uint32_t or a 4-vector of them.
+template <typename V, int LV>
+__device__ inline V vote_group(const V* __restrict__ src, int64_t stride, int M, V (&cnt)[LV]) {
 #pragma unroll
-  for (int l = 0; l < 16; ++l) cnt[l] = V{} ^ V{};
+  for (int l = 0; l < LV; ++l) cnt[l] = V{} ^ V{};
+  auto add = [&](V carry) {
+#pragma unroll
+    for (int l = 0; l < LV; ++l) {
+      const V c = cnt[l];
+      cnt[l] = c ^ carry;
+      carry = c & carry;
+    }
+  };
   int k = 0;
   for (; k + 8 <= M; k += 8) {
     V x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) x[u] = src[static_cast<int64_t>(k + u) * stride];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      V carry = x[u];
-#pragma unroll
-      for (int l = 0; l < 16; ++l)
-        if (l < levels) {
-          const V c = cnt[l];
-          cnt[l] = c ^ carry;
-          carry = c & carry;
-        }
-    }
+    for (int u = 0; u < 8; ++u) add(x[u]);
   }
-  for (; k < M; ++k) {
-    V carry = src[static_cast<int64_t>(k) * stride];
-#pragma unroll
-    for (int l = 0; l < 16; ++l)
-      if (l < levels) {
-        const V c = cnt[l];
-        cnt[l] = c ^ carry;
-        carry = c & carry;
-      }
-  }
-  // count >= T with T = ceil(M/2) <=> carry out of count + (2^levels - T)
-  const uint32_t addend = (1u << levels) - static_cast<uint32_t>((M + 1) >> 1);
+  for (; k < M; ++k) add(src[static_cast<int64_t>(k) * stride]);
+  // count >= T with T = ceil(M/2) <=> carry out of count + (2^LV - T)
+  const uint32_t addend = (1u << LV) - static_cast<uint32_t>((M + 1) >> 1);
   V carry = V{} ^ V{};
 #pragma unroll
-  for (int l = 0; l < 16; ++l)
-    if (l < levels) {
-      const V kbits = V{} ^ V{} ^ (((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u);
-      carry = (cnt[l] & kbits) | ((cnt[l] ^ kbits) & carry);
-    }
+  for (int l = 0; l < LV; ++l) {
+    const V kbits = V{} ^ V{} ^ (((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u);
+    carry = (cnt[l] & kbits) | ((cnt[l] ^ kbits) & carry);
+  }
   return carry;
 }
 
-// int8 sums 2*count - M of the n (<= 32) elements of one word from its bit planes.
-__device__ inline void vote_sums(const uint32_t (&planes)[16], int levels, int M, int n, int8_t* dst) {
+// int8 sums 2*count - M of the n (<= 32) elements of one word, word q of the group,
+// from the counter's bit planes.
+template <typename V, int LV>
+__device__ inline void vote_sums(const V (&cnt)[LV], int q, int M, int n, int8_t* dst) {
+  uint32_t planes[LV];
+#pragma unroll
+  for (int l = 0; l < LV; ++l) planes[l] = lane_word(cnt[l], q);
   for (int b = 0; b < n; ++b) {
     int c = 0;
 #pragma unroll
-    for (int l = 0; l < 16; ++l)
-      if (l < levels) c |= static_cast<int>((planes[l] >> b) & 1u) << l;
+    for (int l = 0; l < LV; ++l) c |= static_cast<int>((planes[l] >> b) & 1u) << l;
     dst[b] = static_cast<int8_t>(2 * c - M);
   }
 }
 
 // One thread per 4 packed words (16-byte loads) when the buffers allow it, else one
-// per word.  Pad bits of the last word are cleared.
-__global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M,
-                                                   int levels, int64_t numel, int64_t nwords,
-                                                   uint32_t* __restrict__ out,
+// per word.  Pad bits of the last word are cleared.  LV bit planes count up to
+// 2^LV - 1 workers; SUMS also writes the int8 sums.
+template <int LV, bool SUMS>
+__global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M, int64_t numel,
+                                                   int64_t nwords, uint32_t* __restrict__ out,
                                                    int8_t* __restrict__ out_sum, int quad) {
-  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int width = quad ? 4 : 1;
-  const int64_t w0 = t * width;
-  if (w0 >= nwords) return;
-  uint32_t words[4], planes[4][16];
-  int nw = 1;
-  if (quad && w0 + 4 <= nwords) {
-    u32x4v cnt[16];
-    const u32x4v v = vote_group<u32x4v>(reinterpret_cast<const u32x4v*>(packed + w0), nwords / 4, M, levels, cnt);
+  auto finish = [&](int64_t w, uint32_t word) {
+    const int64_t tail = numel - w * 32;
+    out[w] = tail < 32 ? word & ((1u << tail) - 1u) : word;
+  };
+  if (quad) {
+    // nwords % 4 == 0: every thread below nwords / 4 owns four whole words
+    const int64_t w0 = t * 4;
+    if (w0 >= nwords) return;
+    u32x4_t cnt[LV];
+    const u32x4_t v = vote_group<u32x4_t, LV>(reinterpret_cast<const u32x4_t*>(packed + w0), nwords / 4, M, cnt);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      words[q] = v[q];
-#pragma unroll
-      for (int l = 0; l < 16; ++l) planes[q][l] = cnt[l][q];
+      finish(w0 + q, v[q]);
+      if (SUMS) {
+        const int64_t tail = numel - (w0 + q) * 32;
+        vote_sums<u32x4_t, LV>(cnt, q, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + (w0 + q) * 32);
+      }
     }
-    nw = 4;
   } else {
-    nw = static_cast<int>(nwords - w0 < width ? nwords - w0 : width);
-    for (int q = 0; q < nw; ++q) {
-      uint32_t cnt[16];
-      words[q] = vote_group<uint32_t>(packed + w0 + q, nwords, M, levels, cnt);
-#pragma unroll
-      for (int l = 0; l < 16; ++l) planes[q][l] = cnt[l];
+    if (t >= nwords) return;
+    uint32_t cnt[LV];
+    finish(t, vote_group<uint32_t, LV>(packed + t, nwords, M, cnt));
+    if (SUMS) {
+      const int64_t tail = numel - t * 32;
+      vote_sums<uint32_t, LV>(cnt, 0, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + t * 32);
     }
-  }
-  for (int q = 0; q < nw; ++q) {
-    const int64_t w = w0 + q;
-    uint32_t valid = 0xFFFFFFFFu;
-    const int64_t tail = numel - w * 32;
-    if (tail < 32) valid = (1u << tail) - 1u;
-    out[w] = words[q] & valid;
-    if (out_sum) vote_sums(planes[q], levels, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + w * 32);
   }
 }
 

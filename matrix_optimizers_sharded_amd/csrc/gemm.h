@@ -100,7 +100,6 @@ __device__ inline int swz(int r) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (gfx9 layout): 48-bit base, stride 0, size in bytes, flags.
 __device__ inline i32x4_t buffer_rsrc(const void* p, uint32_t bytes) {
@@ -560,80 +559,63 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         };
         // A[j][ib..ib+3]: four consecutive k of one row, inside one k-block
         auto load_e = [&](int ib, int j) { return *at<const v4_t>(Ain, kb_off<T>(j, ib, d.pM)); };
-        if (diag) {
-          // diagonal tile: the upper triangle only, with its mirror, so the two halves
-          // hold the same rounded values
+        unsigned char* stg = staging + wave * 4096;
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
+        for (int p = 0; p < 4 / AP; ++p)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-                const int j = j0 + wn + b * 32 + l32;
-                v4_t e = {};
-                if (MODE == GM_POLY) e = load_e(ib, j);
-                float v[4];
-                values(a, b, g, ib, j, e, v);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const int i = ib + t;
-                  if (i <= j) {
-                    const T x = from_f32<T>(v[t]);
-                    store_ws(at<T>(Cr, kb_off<T>(i, j, pr)), x);
-                    store_ws(at<T>(Cr, kb_off<T>(j, i, pr)), x);
-                  }
-                }
-              }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        } else {
-          unsigned char* stg = staging + wave * 4096;
-#pragma unroll
-          for (int p = 0; p < 4 / AP; ++p)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              const int j = j0 + wn + b * 32 + l32;
-              v4_t e[AP][4];
-              if (MODE == GM_POLY) {
-#pragma unroll
-                for (int ap = 0; ap < AP; ++ap)
-#pragma unroll
-                  for (int g = 0; g < 4; ++g) e[ap][g] = load_e(i0 + wm + (AP * p + ap) * 32 + 8 * g + 4 * half, j);
-              }
+          for (int b = 0; b < NB; ++b) {
+            const int j = j0 + wn + b * 32 + l32;
+            v4_t e[AP][4];
+            if (MODE == GM_POLY) {
 #pragma unroll
               for (int ap = 0; ap < AP; ++ap)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  const int a = AP * p + ap;
-                  const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-                  float v[4];
-                  values(a, b, g, ib, j, e[ap][g], v);
-                  // rows ib..ib+3 of column j: consecutive rows of one k-block are
-                  // ROW_BYTES apart, and a half-wave writes 64 contiguous bytes per row
-                  const uint32_t o = kb_off<T>(ib, j, pr);
-#pragma unroll
-                  for (int t = 0; t < 4; ++t) store_ws(at<T>(Cr, o + t * ROW_BYTES), from_f32<T>(v[t]));
-                  const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-                  const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the staged row
-                  *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
-                }
-              // the wave's own LDS accesses execute in order: these reads see the writes
-              // above, and the next round's writes come after them
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int jr = (lane >> 3) + 8 * r, c = lane & 7;
-                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
-                // 16 bytes of row j of C^T, from column i0 + wm + 32 AP p + c (16 / es)
-                // on; the 8 lanes of row j fill one whole k-block row (with 64-byte
-                // k-blocks, rows j and j + 1, j even, share the line)
-                const uint32_t jrow = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
-                const uint32_t icol = static_cast<uint32_t>(i0 + wm + 32 * AP * p) + c * (16 / sizeof(T));
-                store_ws(at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)), w);
-              }
-              __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
+                for (int g = 0; g < 4; ++g) e[ap][g] = load_e(i0 + wm + (AP * p + ap) * 32 + 8 * g + 4 * half, j);
             }
-        }
+#pragma unroll
+            for (int ap = 0; ap < AP; ++ap)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int a = AP * p + ap;
+                const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+                float v[4];
+                values(a, b, g, ib, j, e[ap][g], v);
+                // rows ib..ib+3 of column j: consecutive rows of one k-block are
+                // ROW_BYTES apart, and a half-wave writes 64 contiguous bytes per row
+                const uint32_t o = kb_off<T>(ib, j, pr);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (!diag || ib + t <= j) store_ws(at<T>(Cr, o + t * ROW_BYTES), from_f32<T>(v[t]));
+                const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+                const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the staged row
+                *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
+              }
+            // the wave's own LDS accesses execute in order: these reads see the writes
+            // above, and the next round's writes come after them
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int jr = (lane >> 3) + 8 * r, c = lane & 7;
+              const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
+              // 16 bytes of row j of C^T, from column i0 + wm + 32 AP p + c (16 / es)
+              // on; the 8 lanes of row j fill one whole k-block row (with 64-byte
+              // k-blocks, rows j and j + 1, j even, share the line)
+              const uint32_t jrow = static_cast<uint32_t>(j0 + wn + b * 32 + jr);
+              const uint32_t icol = static_cast<uint32_t>(i0 + wm + 32 * AP * p) + c * (16 / sizeof(T));
+              constexpr uint32_t EPV = 16 / sizeof(T);   // elements per 16-byte piece
+              if (!diag || icol + EPV <= jrow) {
+                store_ws(at<u32x4_t>(Ct, kb_off<T>(jrow, icol, pt)), w);
+              } else if (icol < jrow) {
+                // the piece that straddles the diagonal: only the mirrors of upper
+                // elements (i < j), one by one
+                T x[EPV];
+                __builtin_memcpy(x, &w, 16);
+#pragma unroll
+                for (uint32_t e = 0; e < EPV; ++e)
+                  if (icol + e < jrow) store_ws(at<T>(Ct, kb_off<T>(jrow, icol + e, pt)), x[e]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
+          }
       } else {
         const gptr<TO> out = global(static_cast<TO*>(d.out));
         const int m = d.m, n = d.n;

@@ -438,12 +438,22 @@ int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* ou
   const int64_t threads = quad ? nwords / 4 : nwords;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
-  int levels = 0;
-  while ((1 << levels) <= M) ++levels;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  // the counter needs 2^LV > M: 4 bit planes up to 15 workers, 8 up to 255, else 16
   return launch(PK_VOTE, stream, [&] {
-    hipLaunchKernelGGL(k_sign_vote, dim3(blocks), dim3(256), 0, stream, packed, M, levels, numel, nwords,
-                       out_packed, out_sum, quad);
+#define MO_VOTE(LV, SUMS)                                                                          \
+  hipLaunchKernelGGL((k_sign_vote<LV, SUMS>), dim3(blocks), dim3(256), 0, stream, packed, M, numel, nwords, \
+                     out_packed, out_sum, quad)
+    if (out_sum) {
+      if (M <= 15) MO_VOTE(4, true); else MO_VOTE(8, true);   // sums need M <= 127
+    } else if (M <= 15) {
+      MO_VOTE(4, false);
+    } else if (M <= 255) {
+      MO_VOTE(8, false);
+    } else {
+      MO_VOTE(16, false);
+    }
+#undef MO_VOTE
   });
 }
 

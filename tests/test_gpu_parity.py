@@ -59,7 +59,7 @@ def test_sign_pack_unaligned_view(gpu):
     np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), oracle.sign_pack(v[1:]))
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 127])
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 15, 16, 127])
 @pytest.mark.parametrize("numel", [1, 33, 1000, 65537])
 def test_sign_vote_bit_exact(gpu, M, numel):
     import torch
@@ -87,10 +87,11 @@ def test_sign_vote_large_M_without_sums(gpu):
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), oracle.majority_vote(packed, numel)[0])
 
 
-@pytest.mark.parametrize("M", [5, 1000])
+@pytest.mark.parametrize("M", [5, 15, 16, 255, 256, 1000])
 def test_sign_vote_four_word_path(gpu, M):
     """nwords a multiple of 4 on a 16-byte aligned buffer takes the 4-words-per-thread
-    path; the same words on a base shifted by one word take the one-word path."""
+    path; the same words on a base shifted by one word take the one-word path.  The M
+    values straddle the counter depths (4 bit planes up to 15 workers, 8 up to 255)."""
     import torch
     from matrix_optimizers_sharded_amd import sign_vote
     numel = 1024 * 32 - 3
