@@ -45,11 +45,11 @@ def ns_flops(shapes, iters):
 def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
     """Algorithmic HBM bytes per step of the streaming kernels.
     momentum_sumsq: read G and M, write M (or read x only); prep_operand: read M,
-    write X and X^T in the compute dtype."""
+    write X in the compute dtype."""
     numel = sum(r * c for r, c in shapes)
     mom = numel * (grad_bytes + 8) if momentum else numel * grad_bytes
     src = 4 if momentum else grad_bytes
-    return {"momentum_sumsq": mom, "prep_operand": numel * (src + 2 * compute_bytes)}
+    return {"momentum_sumsq": mom, "prep_operand": numel * (src + compute_bytes)}
 
 
 def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):

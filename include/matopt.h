@@ -83,10 +83,10 @@ typedef struct {
 
 /* Bytes of device workspace muon_step_batched / ns_orthogonalize need for this
  * list with this compute dtype (MO_F32 or MO_BF16).  Returns 0 if the list is
- * invalid (then mo_last_error() says why).  The workspace holds, per matrix, the
- * iterate X and two copies of X^T (ping-pong), A and B, each padded to multiples
- * of 256 in both dimensions, plus the per-call descriptor table and the per-matrix
- * norm partial sums. */
+ * invalid (then mo_last_error() says why).  The workspace holds, per matrix, two
+ * copies of the iterate X (ping-pong), A and B, each padded to multiples of 256 in
+ * both dimensions, plus the per-call descriptor table and the per-matrix norm
+ * partial sums. */
 size_t muon_workspace_bytes(const mo_matrix *mats, int32_t count, int32_t compute_dtype);
 
 /* The owner-local Muon step on `count` matrices, batched: for each matrix

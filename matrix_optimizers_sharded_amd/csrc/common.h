@@ -27,7 +27,7 @@ enum Kind {
 constexpr int GEMM_TILE = 256;   // workspace dims are padded to multiples of this
 constexpr int PREP_TILE = 64;
 constexpr int CHUNK = 4096;      // elements per momentum / sum-of-squares block
-// Workspace operands (X, X^T, A, B) are k-blocked: a buffer of R rows and K columns
+// Workspace operands (X, A, B) are k-blocked: a buffer of R rows and K columns
 // (K, the reduction index of the GEMM that reads it) is stored as K / kb blocks of R
 // rows x KB_BYTES, one after another.  Element (r, k) then sits at byte
 //   (k / kb) * pitch + r * KB_BYTES + (k % kb) * es,   kb = KB_BYTES / es elements,
@@ -56,19 +56,20 @@ struct MatDesc {
   int64_t rows, cols, numel;
   // oriented problem: X is m x n with m = min(rows, cols), n = max(rows, cols)
   int32_t m, n, mp, np;   // mp, np: m and n rounded up to GEMM_TILE
-  uint32_t pX, pT, pM;    // k-block pitch (bytes) of X (mp rows), X^T (np rows), A and B (mp rows)
+  uint32_t pX, pM;        // k-block pitch (bytes) of X and of A, B (mp rows each)
   int32_t transposed;     // 1 if rows > cols (X = M^T)
   int32_t vec_ok;         // 1 if grad/mom/out allow 16-byte vector access
   // workspace buffers, compute dtype, k-blocked (see kb_off), zero outside the m x n
   // corner
-  void* X;                // mp x np (k = column), updated in place by the apply step
-  void* XT[2];            // np x mp (k = column), ping-pong (read by apply as its B operand)
+  void* X[2];             // mp x np (k = column), ping-pong: iteration t reads X[t % 2]
+                          // (SYRK's operands, APPLY's second operand) and APPLY writes
+                          // X[(t + 1) % 2]
   void* A;                // mp x mp, symmetric
   void* B;                // mp x mp, symmetric
   int64_t begin[NKIND];   // first work item of this matrix per launch kind
   int64_t items[NKIND];   // work items of this matrix per launch kind
   int32_t scale_slot;     // index into the per-matrix scale array
-  int32_t pad_[2];
+  int32_t pad_[3];
 };
 
 // Global-address-space view of a device pointer.  Accesses through it compile to

@@ -103,10 +103,10 @@ __global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ 
 }
 
 // Pass 2, one 64x64 tile of the padded oriented operand per block: X = S * scale
-// (S = the updated momentum, or the input), written as X (mp x np) and X^T
-// (np x mp) in the compute dtype, zero outside the m x n corner.  The source tile
-// is read along its contiguous dimension and both outputs are written along theirs,
-// through an LDS tile.
+// (S = the updated momentum, or the input), written as X (mp x np) in the compute
+// dtype, zero outside the m x n corner.  The source tile is read along its
+// contiguous dimension and X is written along its own, through an LDS tile (the
+// source is the transpose of X when rows > cols).
 // Eight consecutive values stored with 16-byte stores (the address is 16-byte
 // aligned: workspace rows are multiples of 128 bytes and b is a multiple of 8).
 template <typename T>
@@ -173,24 +173,19 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
     }
   }
   __syncthreads();
-  // eight consecutive outputs per thread and store: a row of X (X[i0 + a][j0 + b ..])
-  // and a row of X^T (X^T[j0 + a][i0 + b ..] = X[i0 + b ..][j0 + a]); the padded
-  // tile (+1 column) keeps the column reads free of bank conflicts.  Both buffers are
-  // k-blocked along their columns, and eight consecutive columns from a multiple of
-  // 8 never straddle a k-block.
-  unsigned char* const X = static_cast<unsigned char*>(d.X);
-  unsigned char* const XT = static_cast<unsigned char*>(d.XT[0]);
+  // eight consecutive outputs per thread and store: a row piece X[i0 + a][j0 + b ..]
+  // (a column piece of the tile when the source is transposed; the padded tile, +1
+  // column, keeps those reads free of bank conflicts).  X is k-blocked along its
+  // columns, and eight consecutive columns from a multiple of 8 never straddle a
+  // k-block.
+  unsigned char* const X = static_cast<unsigned char*>(d.X[0]);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int a = (t >> 3) + 32 * q, b = (t & 7) * 8;
-    float vx[8], vt[8];
+    float vx[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];
-      vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];
-    }
+    for (int k = 0; k < 8; ++k) vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];
     store8<TC>(global(reinterpret_cast<TC*>(X + kb_off<TC>(i0 + a, j0 + b, d.pX))), vx);
-    store8<TC>(global(reinterpret_cast<TC*>(XT + kb_off<TC>(j0 + a, i0 + b, d.pT))), vt);
   }
 }
 

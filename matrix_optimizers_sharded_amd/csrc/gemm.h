@@ -98,6 +98,22 @@ __device__ inline int swz(int r) {
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// Swizzle of the [k][n] slabs of APPLY's second operand (rows k of 128 bytes of n):
+// a transposing read by 32 lanes covers 64 bytes of each of 4 consecutive rows, and
+// rows k and k + 2 share banks unless their halves are swapped.
+__device__ inline int swz_tr(int k) { return ((k >> 1) & 1) << 2; }
+
+// Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives in slot e the 16-bit element at (the address that lane
+// 4e + i/4 supplied) + (i % 4) elements.  So if lane 16g + 4e + q points at row
+// r0 + e, columns c0 + 4q .. c0 + 4q + 3 of a row-major 16-bit tile, lane 16g + i
+// receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ inline bf16x4_t lds_read_tr16(const unsigned char* p) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(p));
+  return __builtin_bit_cast(bf16x4_t, v);
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -281,8 +297,9 @@ __device__ inline void store4(gptr<T> p, float v0, float v1, float v2, float v3)
 struct TileRef {
   int di, ti, tj, nk;   // descriptor index, tile row and column, k slabs
   i32x4_t rP, rQ;
-  uint32_t vP0, vQ0;    // this lane's byte offsets in k-block 0 of P and Q
-  uint32_t kP, kQ;      // k-block pitch (bytes) of P and Q: the step from slab to slab
+  uint32_t vP0, vQ0;    // this lane's byte offsets of its first load of slab 0 of P and Q
+  uint32_t kP, kQ;      // byte step from one slab to the next, in P and in Q
+  uint32_t qQ;          // byte step from one of a wave's Q loads to the next
 };
 
 // Persistent kernel: the grid holds at most one block per CU, and block b walks the
@@ -305,7 +322,6 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = (wave / WAVES_N) * 128, wn = (wave % WAVES_N) * WAVE_N;
-  const uint32_t esz = sizeof(T);
 
   // Direct-to-LDS loads: wave w, instruction q fills ROWS_PER_INST rows starting at
   // ROWS_PER_INST*(NWAVES*q+w) of an operand slab, 1 KiB contiguous in LDS (lane l ->
@@ -315,6 +331,24 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // base offset per operand plus a uniform stride per instruction.
   const int row0 = ROWS_PER_INST * wave + lane / CHUNKS;
   const uint32_t lane_chunk = ((lane % CHUNKS) ^ swz(row0)) << 4;
+  // rows advance by ROWS_PER_INST * NWAVES from one of a wave's loads to the next
+  constexpr uint32_t VSTEP = ROWS_PER_INST * NWAVES * ROW_BYTES;
+
+  // APPLY's second operand is X itself: X'[i][j] = sum_k B'[i][k] X[k][j].  Its slab
+  // is rows k of the slab's k range and the tile's 256 columns j, which in X's
+  // k-blocked layout are JB = 256 / KB k-blocks, each holding the KR = KB rows as one
+  // contiguous run of KR x 128 bytes.  LDS keeps them as [JB][KR][128 bytes] (16-byte
+  // chunks swizzled by swz_tr(k)), and the MFMA's second operand, 8 consecutive k of
+  // one column per lane, comes out of transposing reads.  Wave w's load q covers 8
+  // rows of k-block (NWAVES q + w) / RG, from row ((NWAVES q + w) % RG) * 8.
+  constexpr bool QT = MODE == GM_APPLY || MODE == GM_APPLY_FINAL || MODE == GM_APPLY_WEIGHT;
+  constexpr int KB = ROW_BYTES / static_cast<int>(sizeof(T));   // elements per k-block
+  constexpr int KR = KB;                                         // k rows per slab
+  constexpr int JB = GT / KB;                                    // k-blocks per tile width
+  constexpr int RG = KR / 8;                                     // 8-row groups per k-block
+  static_assert(ROW_BYTES == 128 && NWAVES % RG == 0, "transposed slab layout assumes 128-byte k-blocks");
+  const int qrow = (wave % RG) * 8 + lane / 8;   // k row of this lane's loads within the slab
+  const uint32_t qlane = static_cast<uint32_t>(qrow) * ROW_BYTES + (((lane % 8) ^ swz_tr(qrow)) << 4);
 
   auto setup = [&](int64_t v, TileRef& t) {
     const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(v, total) : v;
@@ -327,7 +361,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     int K;
     if (MODE == GM_SYRK) {
       upper_tile(local, d->mp / GT, t.ti, t.tj);
-      P = Q = static_cast<const T*>(d->X);
+      P = Q = static_cast<const T*>(d->X[parity]);
       kP = kQ = d->pX;
       K = d->np;
     } else if (MODE == GM_POLY) {
@@ -338,29 +372,37 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     } else {
       rect_tile(local, d->mp / GT, d->np / GT, t.ti, t.tj);
       P = static_cast<const T*>(d->B);
-      Q = static_cast<const T*>(d->XT[parity]);
+      Q = static_cast<const T*>(d->X[parity]);
       kP = d->pM;
-      kQ = d->pT;
+      kQ = d->pX;
       K = d->mp;
     }
     t.di = di;
-    t.nk = K / (ROW_BYTES / static_cast<int>(sizeof(T)));   // >= 512 / ROW_BYTES >= NSTAGE: K >= 256
+    t.nk = K / KB;   // >= 512 / ROW_BYTES >= NSTAGE: K >= 256
     t.rP = buffer_rsrc(P, t.nk * kP);
-    t.rQ = buffer_rsrc(Q, t.nk * kQ);
     t.vP0 = static_cast<uint32_t>(t.ti * GT + row0) * ROW_BYTES + lane_chunk;
-    t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * ROW_BYTES + lane_chunk;
     t.kP = kP;
-    t.kQ = kQ;
+    if (QT) {
+      // the tile's columns j are the JB k-blocks tj * JB .. of X; the slab's k range
+      // is rows kt * KR .. of each
+      t.rQ = buffer_rsrc(Q, static_cast<uint32_t>(d->np / KB) * kQ);
+      t.vQ0 = static_cast<uint32_t>(t.tj * JB + wave / RG) * kQ + qlane;
+      t.kQ = KR * ROW_BYTES;
+      t.qQ = (NWAVES / RG) * kQ;
+    } else {
+      t.rQ = buffer_rsrc(Q, t.nk * kQ);
+      t.vQ0 = static_cast<uint32_t>(t.tj * GT + row0) * ROW_BYTES + lane_chunk;
+      t.kQ = kQ;
+      t.qQ = VSTEP;
+    }
   };
   static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND % 4 == 0, "loads per operand per wave: 2 or 4k");
-  // rows advance by ROWS_PER_INST * NWAVES from one of a wave's loads to the next
-  constexpr uint32_t VSTEP = ROWS_PER_INST * NWAVES * ROW_BYTES;
   auto issue = [&](const TileRef& t, int kt, int stage) {
     const uint32_t sp = kt * t.kP, sq = kt * t.kQ;   // k-block kt of P and of Q
     const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
     if (INST_PER_OPERAND == 2) {
       const uint32_t l[4] = {base, base + NWAVES * 1024, base + OPERAND_BYTES, base + OPERAND_BYTES + NWAVES * 1024};
-      const uint32_t v[4] = {t.vP0, t.vP0 + VSTEP, t.vQ0, t.vQ0 + VSTEP};
+      const uint32_t v[4] = {t.vP0, t.vP0 + VSTEP, t.vQ0, t.vQ0 + t.qQ};
       load_lds16_2x2(t.rP, t.rQ, l, v, sp, sq);
     } else {
 #pragma unroll
@@ -371,7 +413,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           lp[q] = base + (q0 + q) * NWAVES * 1024;
           lq[q] = lp[q] + OPERAND_BYTES;
           vp[q] = t.vP0 + (q0 + q) * VSTEP;
-          vq[q] = t.vQ0 + (q0 + q) * VSTEP;
+          vq[q] = t.vQ0 + (q0 + q) * t.qQ;
         }
         load_lds16x4(t.rP, lp, vp, sp);
         load_lds16x4(t.rQ, lq, vq, sq);
@@ -413,30 +455,68 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
 #ifndef MO_GEMM_INTERLEAVE
 #define MO_GEMM_INTERLEAVE 1
 #endif
+  // LDS reads and MFMAs per k16 step: one 16-byte read per first-operand fragment;
+  // per second-operand fragment one 16-byte read, or (QT) two transposing 8-byte
+  // reads for bf16 and four 4-byte reads for fp32; one MFMA per fragment pair for
+  // bf16, four for fp32
+  constexpr int NREAD = 4 + NB * (QT ? (sizeof(T) == 2 ? 2 : 4) : 1);
+  constexpr int NMFMA = 4 * NB * (sizeof(T) == 2 ? 1 : 4);
+  constexpr int NPAIR = NREAD < NMFMA ? NREAD : NMFMA;
 #if MO_GEMM_INTERLEAVE
 #define MO_STEP_FENCE() do {} while (0)
 #define MO_STEP_INTERLEAVE()                                                   \
   do {                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4 + NB; ++i_) {                    \
+    _Pragma("unroll") for (int i_ = 0; i_ < NPAIR; ++i_) {                     \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* one LDS read */    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */        \
     }                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - 4 - NB, 0);           \
+    if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0); \
+    if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0); \
   } while (0)
 #else
 #define MO_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define MO_STEP_INTERLEAVE() do {} while (0)
 #endif
   frag_t fa[2][4], fb[2][NB];
+  // QT, bf16: lane 16g + 4e + q addresses row 8 (g / 2) + e (plus 16 per k16 step)
+  // and columns 16 (g % 2) + 4q .. + 3 of a 32-column block, so that two
+  // transposing reads (rows +0..3, +4..7) give it 8 consecutive k of column l % 32
+  const int trow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   auto read_frags = [&](const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
     const unsigned char* sQ = sP + OPERAND_BYTES;
     const int c = 2 * kk + half;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       A[a] = *reinterpret_cast<const frag_t*>(sP + rowA[a] * ROW_BYTES + ((c ^ swz(rowA[a])) << 4));
+    if constexpr (!QT) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
+      for (int b = 0; b < NB; ++b)
+        B[b] = *reinterpret_cast<const frag_t*>(sQ + rowB[b] * ROW_BYTES + ((c ^ swz(rowB[b])) << 4));
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int n = wn + 32 * b + tcol;                  // column j - j0 of the tile
+        const int nb = (n % KB) * 2, k = 16 * kk + trow;   // byte in the k-block row; k row
+        const unsigned char* q =
+            sQ + (n / KB) * (KR * ROW_BYTES) + k * ROW_BYTES + ((((nb >> 4) ^ swz_tr(k)) << 4) | (nb & 15));
+        const bf16x4_t lo = lds_read_tr16(q), hi = lds_read_tr16(q + 4 * ROW_BYTES);   // swz_tr(k + 4) == swz_tr(k)
+        B[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    } else {
+      // fp32: lane l needs rows 4c .. 4c + 3 (the k of its first-operand chunk) of
+      // column l % 32, four 4-byte reads
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int n = wn + 32 * b + l32, nb = (n % KB) * 4;
+        const unsigned char* col = sQ + (n / KB) * (KR * ROW_BYTES);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * c + e;
+          B[b][e] = *reinterpret_cast<const float*>(col + k * ROW_BYTES + ((((nb >> 4) ^ swz_tr(k)) << 4) | (nb & 15)));
+        }
+      }
+    }
   };
   auto mfma_step = [&](const frag_t* A, const frag_t* B) {
 #pragma unroll
@@ -533,10 +613,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         gptr<T> Cr, Ct;
         uint32_t pr, pt;
         if (MODE == GM_APPLY) {
-          Cr = global(static_cast<T*>(d.X));
-          pr = d.pX;
-          Ct = global(static_cast<T*>(d.XT[parity ^ 1]));
-          pt = d.pT;
+          // X' into the other ping-pong buffer (other tiles still read X); no
+          // transposed copy
+          Cr = Ct = global(static_cast<T*>(d.X[parity ^ 1]));
+          pr = pt = d.pX;
         } else {
           Cr = Ct = global(static_cast<T*>(MODE == GM_SYRK ? d.A : d.B));
           pr = pt = d.pM;
@@ -586,6 +666,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                   if (!diag || ib + t <= j) store_ws(at<T>(Cr, o + t * ROW_BYTES), from_f32<T>(v[t]));
+                if (MODE == GM_APPLY) continue;
                 const v4_t w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
                 const int off = (32 * ap + 8 * g + 4 * half) * static_cast<int>(ES);   // within the staged row
                 *reinterpret_cast<v4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
@@ -594,6 +675,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             // above, and the next round's writes come after them
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
+              if (MODE == GM_APPLY) break;
               const int jr = (lane >> 3) + 8 * r, c = lane & 7;
               const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
               // 16 bytes of row j of C^T, from column i0 + wm + 32 AP p + c (16 / es)

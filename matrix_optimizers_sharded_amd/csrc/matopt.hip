@@ -108,27 +108,24 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.np = static_cast<int32_t>(round_up(d.n, GEMM_TILE));
     d.vec_ok = (aligned16(d.grad) && aligned16(d.mom) && aligned16(d.out) && (mt.cols % 4 == 0)) ? 1 : 0;
     d.scale_slot = k;
-    // k-blocked operands: np / kb blocks of mp rows (X), mp / kb blocks of np rows
-    // (X^T), mp / kb blocks of mp rows (A, B); mp and np are multiples of kb
+    // k-blocked operands: np / kb blocks of mp rows (X), mp / kb blocks of mp rows
+    // (A, B); mp and np are multiples of kb
     const size_t kb = KB_BYTES / es;
     const size_t xb = size_t(d.np) / kb * size_t(d.mp) * KB_BYTES;
-    const size_t tb = size_t(d.mp) / kb * size_t(d.np) * KB_BYTES;
     const size_t ab = size_t(d.mp) / kb * size_t(d.mp) * KB_BYTES;
     // the GEMM addresses each operand buffer with 32-bit byte offsets
-    if (xb > size_t(0x7fffffff) || tb > size_t(0x7fffffff))
+    if (xb > size_t(0x7fffffff))
       return fail(MO_ERR_UNSUPPORTED, "matrix " + std::to_string(order[k]) +
                                           ": padded operand exceeds 2 GiB (min(rows,cols) * max(rows,cols))");
     d.pX = static_cast<uint32_t>(d.mp) * KB_BYTES;
-    d.pT = static_cast<uint32_t>(d.np) * KB_BYTES;
     d.pM = static_cast<uint32_t>(d.mp) * KB_BYTES;
     auto take = [&](size_t nb) {
       void* p = base ? static_cast<void*>(base + off) : nullptr;
       off = align_up(off + nb, ALIGN);
       return p;
     };
-    d.X = take(xb);
-    d.XT[0] = take(tb);
-    d.XT[1] = take(tb);
+    d.X[0] = take(xb);
+    d.X[1] = take(xb);
     d.A = take(ab);
     d.B = take(ab);
     const int64_t tm = d.mp / GEMM_TILE, tn = d.np / GEMM_TILE;
