@@ -27,18 +27,15 @@ enum Kind {
 constexpr int GEMM_TILE = 256;   // workspace dims are padded to multiples of this
 constexpr int PREP_TILE = 64;
 constexpr int CHUNK = 4096;      // elements per momentum / sum-of-squares block
-// Workspace operands (X, A, B) are k-blocked: a buffer of R rows and K columns
-// (K, the reduction index of the GEMM that reads it) is stored as K / kb blocks of R
+// Workspace operands (X, A, B) are k-blocked: a buffer of R rows and K columns (K,
+// the reduction index of the GEMM that reads it) is stored as K / kb blocks of R
 // rows x KB_BYTES, one after another.  Element (r, k) then sits at byte
 //   (k / kb) * pitch + r * KB_BYTES + (k % kb) * es,   kb = KB_BYTES / es elements,
 // pitch = R * KB_BYTES.  The k-slab of 256 rows that one GEMM step consumes is one
 // contiguous 32 KiB run instead of 256 row pieces spread over megabytes: 2-3% less
 // GEMM time than row-major operands with a padded pitch.  (64-byte blocks, which
 // leave room for a four-slab LDS ring of whole lines, measured no faster.)
-#ifndef MO_GEMM_SLAB_BYTES
-#define MO_GEMM_SLAB_BYTES 128
-#endif
-constexpr int KB_BYTES = MO_GEMM_SLAB_BYTES;
+constexpr int KB_BYTES = 128;
 
 // Byte offset of element (r, k) of a k-blocked buffer whose k-blocks are `pitch`
 // bytes apart.  Workspace buffers stay below 2 GiB, so 32 bits hold every offset.

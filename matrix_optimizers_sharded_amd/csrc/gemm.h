@@ -40,13 +40,11 @@ enum GemmMode { GM_SYRK = 0, GM_POLY = 1, GM_APPLY = 2, GM_APPLY_FINAL = 3, GM_A
 constexpr int GT = GEMM_TILE;          // 256
 
 // k-slab geometry: each operand row of a slab is ROW_BYTES, one k-block of the
-// workspace layout (128: 64 bf16 / 32 fp32 of k), and NSTAGE slabs are in flight in
-// an LDS ring, so the loads of slab t+NSTAGE-1 overlap the MFMAs of slabs t ..
-// t+NSTAGE-2.  (With 64-byte blocks the ring holds four 32 KiB stages, three slabs
-// of load cover instead of one; the extra barriers ate the gain.)
-#ifndef MO_GEMM_STAGES
-#define MO_GEMM_STAGES (MO_GEMM_SLAB_BYTES == 64 ? 4 : 2)
-#endif
+// workspace layout (128: 64 bf16 / 32 fp32 of k), and NSTAGE = 2 slabs are in flight
+// in an LDS ring (2 x 64 KiB, with the 32 KiB epilogue staging the whole 160 KiB),
+// so the loads of slab t+1 overlap the MFMAs of slab t.  (A four-stage ring of
+// 64-byte slabs, three slabs of load cover instead of one, measured no faster: the
+// extra barriers ate the gain.)
 // The epilogue's stores into the workspace are non-temporal: they are read again
 // only by the next launch, so they need not displace the operand panels that the
 // other blocks of an XCD are sharing in L2.  Measured: -0.5% time for the staged
@@ -65,7 +63,7 @@ __device__ inline void store_ws(gptr<V> p, const V& v) {
 constexpr int ROW_BYTES = KB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
 constexpr int KSTEPS = CHUNKS / 2;                     // k16 MFMA steps per slab
-constexpr int NSTAGE = MO_GEMM_STAGES;
+constexpr int NSTAGE = 2;
 constexpr int OPERAND_BYTES = GT * ROW_BYTES;
 constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;         // P and Q
 constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
@@ -93,10 +91,7 @@ constexpr int RSRC_FLAGS = 0x00020000;
 // 16-byte chunk swizzle inside a row, chosen so that the fragment reads of 8
 // consecutive rows (32 banks x 4 B) and of 16 consecutive rows (64 banks) fall in
 // distinct banks.
-__device__ inline int swz(int r) {
-  if (CHUNKS == 8) return (r ^ (r >> 1)) & 7;
-  return ((r >> 1) ^ (r >> 3)) & 3;
-}
+__device__ inline int swz(int r) { return (r ^ (r >> 1)) & 7; }
 
 // Swizzle of the [k][n] slabs of APPLY's second operand (rows k of 128 bytes of n):
 // a transposing read by 32 lanes covers 64 bytes of each of 4 consecutive rows, and
@@ -156,33 +151,6 @@ __device__ inline void load_lds16x4(i32x4_t rsrc, const uint32_t (&lds)[4], cons
         "s"(so)
       : "memory");
 }
-// The same for two loads from each of two buffers (P then Q) in one block, with a
-// scalar offset per buffer.
-__device__ inline void load_lds16_2x2(i32x4_t rsrc_p, i32x4_t rsrc_q, const uint32_t (&lds)[4],
-                                      const uint32_t (&voff)[4], uint32_t soff_p, uint32_t soff_q) {
-  i32x4_t rp, rq;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    rp[c] = __builtin_amdgcn_readfirstlane(rsrc_p[c]);
-    rq[c] = __builtin_amdgcn_readfirstlane(rsrc_q[c]);
-  }
-  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds[0]), l1 = __builtin_amdgcn_readfirstlane(lds[1]);
-  const uint32_t l2 = __builtin_amdgcn_readfirstlane(lds[2]), l3 = __builtin_amdgcn_readfirstlane(lds[3]);
-  const uint32_t sp = __builtin_amdgcn_readfirstlane(soff_p), sq = __builtin_amdgcn_readfirstlane(soff_q);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %11 offen lds\n\t"
-      "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %11 offen lds\n\t"
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %10, %12 offen lds\n\t"
-      "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %10, %12 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(l0), "s"(l1), "s"(l2), "s"(l3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rp),
-        "s"(rq), "s"(sp), "s"(sq)
-      : "memory");
-}
-
 __device__ inline uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
 }
@@ -396,28 +364,22 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       t.qQ = VSTEP;
     }
   };
-  static_assert(INST_PER_OPERAND == 2 || INST_PER_OPERAND % 4 == 0, "loads per operand per wave: 2 or 4k");
+  static_assert(INST_PER_OPERAND % 4 == 0, "loads per operand per wave: a multiple of 4");
   auto issue = [&](const TileRef& t, int kt, int stage) {
     const uint32_t sp = kt * t.kP, sq = kt * t.kQ;   // k-block kt of P and of Q
     const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
-    if (INST_PER_OPERAND == 2) {
-      const uint32_t l[4] = {base, base + NWAVES * 1024, base + OPERAND_BYTES, base + OPERAND_BYTES + NWAVES * 1024};
-      const uint32_t v[4] = {t.vP0, t.vP0 + VSTEP, t.vQ0, t.vQ0 + t.qQ};
-      load_lds16_2x2(t.rP, t.rQ, l, v, sp, sq);
-    } else {
 #pragma unroll
-      for (int q0 = 0; q0 < INST_PER_OPERAND; q0 += 4) {
-        uint32_t lp[4], lq[4], vp[4], vq[4];
+    for (int q0 = 0; q0 < INST_PER_OPERAND; q0 += 4) {
+      uint32_t lp[4], lq[4], vp[4], vq[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          lp[q] = base + (q0 + q) * NWAVES * 1024;
-          lq[q] = lp[q] + OPERAND_BYTES;
-          vp[q] = t.vP0 + (q0 + q) * VSTEP;
-          vq[q] = t.vQ0 + (q0 + q) * t.qQ;
-        }
-        load_lds16x4(t.rP, lp, vp, sp);
-        load_lds16x4(t.rQ, lq, vq, sq);
+      for (int q = 0; q < 4; ++q) {
+        lp[q] = base + (q0 + q) * NWAVES * 1024;
+        lq[q] = lp[q] + OPERAND_BYTES;
+        vp[q] = t.vP0 + (q0 + q) * VSTEP;
+        vq[q] = t.vQ0 + (q0 + q) * t.qQ;
       }
+      load_lds16x4(t.rP, lp, vp, sp);
+      load_lds16x4(t.rQ, lq, vq, sq);
     }
   };
 
