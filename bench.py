@@ -94,11 +94,11 @@ def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):
 
 def traffic_of(kind, workload):
     """HBM bytes per launch of `kind` from the committed rocprofv3 counter summary for
-    this workload, or None if there is none or the kernel sources changed since."""
-    from matrix_optimizers_sharded_amd.profsummary import read_traffic, source_hash
+    this workload, or None if there is none or the library's GPU code changed since."""
+    from matrix_optimizers_sharded_amd.profsummary import read_traffic, code_hash
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
     val, h = read_traffic(path, kind)
-    if val is None or h != source_hash():
+    if val is None or h != code_hash():
         return None
     return val
 

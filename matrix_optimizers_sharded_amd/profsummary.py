@@ -8,17 +8,17 @@
 kernel kind).  `pmc` summarises two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
 command that also performs one plain device copy of --copy-bytes (bench.py
 --calibrate-copy): each counter is scaled by what it reads for that copy, giving
-HBM bytes per dispatch.  Both record a hash of the library's kernel sources; the
+HBM bytes per dispatch.  Both record a hash of the library's GPU code objects; the
 benchmark reports the traffic figure only while that hash still matches.
 """
 
 import argparse
 import collections
 import csv
-import glob
 import hashlib
 import os
 import re
+import struct
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
@@ -38,14 +38,34 @@ KINDS = [
 ]
 
 
-def source_hash():
-    """sha256 over the library's kernel sources (csrc/*.h, csrc/*.hip), in name order."""
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*.h")) + glob.glob(os.path.join(PKG, "csrc", "*.hip"))):
-        h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def _elf_section(data, wanted):
+    """Bytes of the section named `wanted` in a little-endian ELF64 image, or None."""
+    if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
+        return None
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def header(i):   # sh_name, sh_type, sh_flags, sh_addr, sh_offset, sh_size, ...
+        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    for i in range(shnum):
+        h = header(i)
+        start = names + h[0]
+        if data[start:data.index(b"\0", start)] == wanted:
+            return data[h[4]:h[4] + h[5]]
+    return None
+
+
+def code_hash(lib=None):
+    """sha256 of the GPU code objects (the .hip_fatbin section) of the built library:
+    it changes when the device code does, not when only comments or host code do."""
+    from matrix_optimizers_sharded_amd.binding import library_path
+    with open(lib or library_path(), "rb") as f:
+        sec = _elf_section(f.read(), b".hip_fatbin")
+    if sec is None:
+        raise RuntimeError("no .hip_fatbin section in the library")
+    return hashlib.sha256(sec).hexdigest()[:16]
 
 
 def kind_of(name):
@@ -67,7 +87,7 @@ def summarize_trace(stats_csv, cmd):
     lines = [
         "# rocprofv3 --kernel-trace --stats summary, per kernel kind",
         f"# command: {cmd}",
-        f"source_sha256 = {source_hash()}",
+        f"code_sha256 = {code_hash()}",
         f"{'kind':<16} {'calls':>7} {'mean_ms':>10} {'total_ms':>10}",
     ]
     for k in sorted(calls, key=lambda k: -total[k]):
@@ -102,7 +122,7 @@ def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes):
         f"# {copy_bytes} bytes in the same run",
         f"# command (fetch): {cmd_fetch}",
         f"# command (write): {cmd_write}",
-        f"source_sha256 = {source_hash()}",
+        f"code_sha256 = {code_hash()}",
         f"copy_bytes = {copy_bytes}",
         f"copy_fetch_kib = {cf:.1f}",
         f"copy_write_kib = {cw:.1f}",
@@ -126,7 +146,7 @@ def read_traffic(path, kind):
         return None, None
     h, val = None, None
     for line in open(path):
-        if line.startswith("source_sha256"):
+        if line.startswith("code_sha256"):
             h = line.split("=")[1].strip()
         parts = line.split()
         if parts and parts[0] == kind and len(parts) == 5:

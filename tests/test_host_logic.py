@@ -93,7 +93,35 @@ def test_profsummary_round_trip(tmp_path):
     val, h = profsummary.read_traffic(str(out), "ns_apply")
     # fetch scale 2, write scale 1; mean of the two APPLY dispatches
     assert val == pytest.approx((2000 * 1024 * 2.0) + (200 * 1024 * 1.0))
-    assert h == profsummary.source_hash()
+    assert h == profsummary.code_hash()
+
+
+def _tiny_elf(payload):
+    """A minimal little-endian ELF64 image with a .hip_fatbin section holding payload."""
+    import struct
+    names = b"\0.hip_fatbin\0.shstrtab\0"
+    data_off = 64
+    names_off = data_off + len(payload)
+    shoff = (names_off + len(names) + 7) // 8 * 8
+    head = bytearray(64)
+    head[:6] = b"\x7fELF\x02\x01"
+    struct.pack_into("<Q", head, 0x28, shoff)
+    struct.pack_into("<HHH", head, 0x3A, 64, 3, 2)
+    sh = lambda name, off, size: struct.pack("<IIQQQQIIQQ", name, 1, 0, 0, off, size, 0, 0, 1, 0)
+    body = bytes(head) + payload + names
+    body += b"\0" * (shoff - len(body))
+    return body + bytes(64) + sh(1, data_off, len(payload)) + sh(13, names_off, len(names))
+
+
+def test_code_hash_reads_the_fatbin_section(tmp_path):
+    a, b = tmp_path / "a.so", tmp_path / "b.so"
+    a.write_bytes(_tiny_elf(b"code object one"))
+    b.write_bytes(_tiny_elf(b"code object two"))
+    assert profsummary._elf_section(a.read_bytes(), b".hip_fatbin") == b"code object one"
+    assert profsummary._elf_section(a.read_bytes(), b".text") is None
+    assert profsummary.code_hash(str(a)) != profsummary.code_hash(str(b))
+    # the built library has one, and its hash is stable
+    assert profsummary.code_hash() == profsummary.code_hash()
 
 
 def _imports(path):
