@@ -2,9 +2,11 @@
 
     python -m matrix_optimizers_sharded_amd.profsummary trace <stats.csv> <out.txt> --cmd "<command>"
     python -m matrix_optimizers_sharded_amd.profsummary pmc <fetch.csv> <write.csv> <out.txt> \
-        --cmd-fetch "<command>" --cmd-write "<command>" [--copy-bytes N]
+        --cmd-fetch "<command>" --cmd-write "<command>" [--copy-bytes N] [--by-size]
+    python -m matrix_optimizers_sharded_amd.profsummary mfma <counters.csv> <out.txt> --cmd "<command>"
 
-`trace` summarises a `--kernel-trace --stats` run (calls and mean duration per
+`mfma` summarises a `--pmc MfmaUtil MfmaFlopsBF16` run (MFMA busy share and counted
+bf16 flops per dispatch).  `trace` summarises a `--kernel-trace --stats` run (calls and mean duration per
 kernel kind).  `pmc` summarises two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
 command that also performs one plain device copy of --copy-bytes (bench.py
 --calibrate-copy): each counter is scaled by what it reads for that copy, giving
@@ -95,7 +97,8 @@ def summarize_trace(stats_csv, cmd):
     return "\n".join(lines) + "\n"
 
 
-def _counter_by_kind(path, counter):
+def _counter_by_kind(path, counter, by_size=False):
+    """Counter values per kernel kind (or per kind and grid size, as kind@grid)."""
     vals = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
@@ -103,13 +106,15 @@ def _counter_by_kind(path, counter):
         k = kind_of(r["Kernel_Name"])
         if k is None:
             continue
+        if by_size and k != "device_copy":
+            k = f"{k}@{r['Grid_Size']}"
         vals[k].append(float(r["Counter_Value"]))
     return vals
 
 
-def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes):
-    fetch = _counter_by_kind(fetch_csv, "FETCH_SIZE")
-    write = _counter_by_kind(write_csv, "WRITE_SIZE")
+def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes, by_size=False):
+    fetch = _counter_by_kind(fetch_csv, "FETCH_SIZE", by_size)
+    write = _counter_by_kind(write_csv, "WRITE_SIZE", by_size)
     if "device_copy" not in fetch or "device_copy" not in write:
         raise SystemExit("no device copy dispatch found for calibration")
     # the runtime may split the calibration copy into several dispatches: sum them
@@ -119,7 +124,7 @@ def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes):
     lines = [
         "# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per",
         "# dispatch), each scaled by what the same counter reads for one plain device copy of",
-        f"# {copy_bytes} bytes in the same run",
+        f"# {copy_bytes} bytes in the same run" + ("; rows are kind@grid size (work-items)" if by_size else ""),
         f"# command (fetch): {cmd_fetch}",
         f"# command (write): {cmd_write}",
         f"code_sha256 = {code_hash()}",
@@ -137,6 +142,46 @@ def summarize_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write, copy_bytes):
         w = sum(write[k]) / len(write[k])
         b = f * 1024.0 * fs + w * 1024.0 * ws
         lines.append(f"{k:<16} {len(fetch[k]):>10} {f:>14.1f} {w:>14.1f} {b:>22.4e}")
+    return "\n".join(lines) + "\n"
+
+
+SIMDS = 1024                                   # 256 CUs x 4 SIMDs
+BF16_FLOP_PER_SIMD_CYCLE = 2.5e15 / (SIMDS * 2.4e9)   # dense bf16 MFMA peak at 2.4 GHz
+
+
+def summarize_mfma(path, cmd):
+    """MfmaUtil (MFMA busy cycles / (active cycles x SIMDs)) and MfmaFlopsBF16 per
+    dispatch, per kernel kind; the clock they imply is the counted flop rate over
+    busy SIMD-cycles at the dense bf16 rate."""
+    disp = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        k = kind_of(r["Kernel_Name"])
+        if k is None or r["Counter_Name"] not in ("MfmaUtil", "MfmaFlopsBF16"):
+            continue
+        d = disp[r["Dispatch_Id"]]
+        d["kind"] = k
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    per = collections.defaultdict(list)
+    for d in disp.values():
+        if "MfmaUtil" in d and "MfmaFlopsBF16" in d:
+            per[d["kind"]].append(d)
+    lines = [
+        "# MFMA utilisation per kernel kind from rocprofv3 --pmc MfmaUtil MfmaFlopsBF16",
+        "# (MfmaUtil = MFMA busy cycles / (GPU active cycles x SIMDs); MfmaFlopsBF16 = 512 x",
+        "# SQ_INSTS_VALU_MFMA_MOPS_BF16); durations are those of the counter run",
+        f"# command: {cmd}",
+        f"code_sha256 = {code_hash()}",
+        f"{'kind':<16} {'dispatches':>10} {'mfma_util_%':>11} {'bf16_flop':>12} {'ms':>9} {'TFLOP/s':>9} {'clock_GHz':>9}",
+    ]
+    for k in sorted(per, key=lambda k: -sum(d["MfmaFlopsBF16"] for d in per[k])):
+        ds = per[k]
+        util = sum(d["MfmaUtil"] for d in ds) / len(ds)
+        flop = sum(d["MfmaFlopsBF16"] for d in ds) / len(ds)
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        rate = flop / (ns * 1e-9) if ns > 0 else 0.0
+        clock = rate / (util / 100.0 * SIMDS * BF16_FLOP_PER_SIMD_CYCLE) / 1e9 if util > 0 else 0.0
+        lines.append(f"{k:<16} {len(ds):>10} {util:>11.2f} {flop:>12.4e} {ns / 1e6:>9.3f} {rate / 1e12:>9.1f} {clock:>9.3f}")
     return "\n".join(lines) + "\n"
 
 
@@ -168,11 +213,18 @@ def main():
     p.add_argument("--cmd-fetch", required=True)
     p.add_argument("--cmd-write", required=True)
     p.add_argument("--copy-bytes", type=int, default=1 << 30)
+    p.add_argument("--by-size", action="store_true", help="one row per kernel kind and grid size")
+    m = sub.add_parser("mfma")
+    m.add_argument("counter_csv")
+    m.add_argument("out")
+    m.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.mode == "trace":
         text = summarize_trace(a.stats_csv, a.cmd)
+    elif a.mode == "mfma":
+        text = summarize_mfma(a.counter_csv, a.cmd)
     else:
-        text = summarize_pmc(a.fetch_csv, a.write_csv, a.cmd_fetch, a.cmd_write, a.copy_bytes)
+        text = summarize_pmc(a.fetch_csv, a.write_csv, a.cmd_fetch, a.cmd_write, a.copy_bytes, a.by_size)
     with open(a.out, "w") as f:
         f.write(text)
     print(text)

@@ -96,6 +96,27 @@ def test_profsummary_round_trip(tmp_path):
     assert h == profsummary.code_hash()
 
 
+def test_profsummary_mfma(tmp_path):
+    path = tmp_path / "m.csv"
+    hdr = "Dispatch_Id,Grid_Size,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    name = "_ZN2mo9k_ns_gemmIDF16bLi2EDF16bEEvPKNS_7MatDescEilifff"
+    # two APPLY dispatches of 2 ms, 60% and 50% busy, 2.0e12 and 1.6e12 counted flops
+    path.write_text(hdr + textwrap.dedent(f"""\
+        1,65536,{name},MfmaUtil,60.0,0,2000000
+        1,65536,{name},MfmaFlopsBF16,2.0e12,0,2000000
+        2,65536,{name},MfmaUtil,50.0,0,2000000
+        2,65536,{name},MfmaFlopsBF16,1.6e12,0,2000000
+        """))
+    text = profsummary.summarize_mfma(str(path), "cmd")
+    row = [ln.split() for ln in text.splitlines() if ln.startswith("ns_apply")][0]
+    assert row[1] == "2" and float(row[2]) == pytest.approx(55.0)
+    assert float(row[3]) == pytest.approx(1.8e12, rel=1e-3)
+    assert float(row[5]) == pytest.approx(900.0, rel=1e-3)          # TFLOP/s
+    # 0.9e15 flop/s over 55% of 1024 SIMDs at the bf16 rate per SIMD-cycle
+    want = 0.9e15 / (0.55 * 1024 * 2.5e15 / (1024 * 2.4e9)) / 1e9
+    assert float(row[6]) == pytest.approx(want, rel=1e-3)
+
+
 def _tiny_elf(payload):
     """A minimal little-endian ELF64 image with a .hip_fatbin section holding payload."""
     import struct
