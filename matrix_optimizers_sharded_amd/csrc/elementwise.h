@@ -42,18 +42,20 @@ template <> __device__ inline f32x4_t load4_f32<bf16_t>(const bf16_t* p) {
 
 // Pass 1, one 4096-element chunk per block.  With MOMENTUM: M <- fma(beta, M, G)
 // in place, and the chunk's sum of M^2 goes to partial[item].  Without: the sum of
-// squares of the input only.
+// squares of the input only.  The squares are summed in fp64: exact products, and
+// no overflow for any finite fp32 value (fp32 squares overflow from |M| ~ 1.8e19);
+// the kernel is bound by HBM, so the fp64 arithmetic costs nothing.
 template <typename TG, bool MOMENTUM>
 __global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restrict__ descs,
                                                         int count, float beta,
-                                                        float* __restrict__ partial) {
+                                                        double* __restrict__ partial) {
   const int64_t item = blockIdx.x;
   const MatDesc& d = descs[find_desc(descs, count, KIND_CHUNK, item)];
   const int64_t e0 = (item - d.begin[KIND_CHUNK]) * CHUNK;
   const int64_t numel = d.numel;
   const TG* __restrict__ g = static_cast<const TG*>(d.grad);
   float* __restrict__ m = d.mom;
-  float ss = 0.f;
+  double ss = 0.0;
   if (d.vec_ok && e0 + CHUNK <= numel) {
     f32x4_t gv[4], mv[4];
 #pragma unroll
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restric
         *reinterpret_cast<f32x4_t*>(m + e0 + q * 1024 + threadIdx.x * 4) = v;
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ss = __builtin_fmaf(v[t], v[t], ss);
+      for (int t = 0; t < 4; ++t) ss = __builtin_fma(static_cast<double>(v[t]), static_cast<double>(v[t]), ss);
     }
   } else {
     const int64_t e1 = (e0 + CHUNK < numel) ? e0 + CHUNK : numel;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restric
         v = __builtin_fmaf(beta, m[e], v);
         m[e] = v;
       }
-      ss = __builtin_fmaf(v, v, ss);
+      ss = __builtin_fma(static_cast<double>(v), static_cast<double>(v), ss);
     }
   }
   ss = block_sum_256(ss);
@@ -92,12 +94,12 @@ __global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restric
 // One block per matrix: scale = 1 / (sqrt(sum of partials) + eps), summed in fp64
 // in a fixed order.
 __global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ descs,
-                                                    const float* __restrict__ partial,
+                                                    const double* __restrict__ partial,
                                                     float eps, float* __restrict__ scale) {
   const MatDesc& d = descs[blockIdx.x];
   double s = 0.0;
-  const float* p = partial + d.begin[KIND_CHUNK];
-  for (int64_t c = threadIdx.x; c < d.items[KIND_CHUNK]; c += 256) s += static_cast<double>(p[c]);
+  const double* p = partial + d.begin[KIND_CHUNK];
+  for (int64_t c = threadIdx.x; c < d.items[KIND_CHUNK]; c += 256) s += p[c];
   s = block_sum_256(s);
   if (threadIdx.x == 0) scale[d.scale_slot] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
 }

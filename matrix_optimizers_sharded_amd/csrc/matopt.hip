@@ -88,7 +88,7 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
   int64_t chunks = 0;
   for (int i = 0; i < count; ++i) chunks += (mats[i].rows * mats[i].cols + CHUNK - 1) / CHUNK;
   plan.off_partial = off;
-  off = align_up(off + sizeof(float) * std::max<int64_t>(chunks, 1), ALIGN);
+  off = align_up(off + sizeof(double) * std::max<int64_t>(chunks, 1), ALIGN);
 
   plan.descs.resize(count);
   for (int k = 0; k < count; ++k) {
@@ -340,7 +340,7 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   MatDesc* dd = reinterpret_cast<MatDesc*>(base + full.off_desc);
   float* scale = reinterpret_cast<float*>(base + full.off_scale);
-  float* partial = reinterpret_cast<float*>(base + full.off_partial);
+  double* partial = reinterpret_cast<double*>(base + full.off_partial);
   MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
 
   MO_TRY(launch(PK_MOM, stream, [&] {

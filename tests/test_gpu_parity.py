@@ -194,6 +194,24 @@ def test_zero_matrix_gives_zero(gpu):
         assert np.all(gu[0] == 0) and np.all(gm[0] == 0)
 
 
+@pytest.mark.parametrize("scale", [2.0 ** 70, 2.0 ** -70])
+def test_extreme_input_scales(gpu, scale):
+    """Inputs near the fp32 range ends: at 2^70 the squares (2^140) overflow fp32, so
+    the Frobenius sum must not be formed in fp32; at 2^-70 the norm falls far below
+    eps and X0 = x / (|x|_F + eps) stays tiny.  Both must follow the oracle."""
+    import torch
+    shapes = [(300, 520), (520, 300)]
+    xs = [(gaussian(s, 700 + i) * np.float32(scale)).astype(np.float32) for i, s in enumerate(shapes)]
+    assert all(np.isfinite(x).all() for x in xs)
+    say(f"extreme scale 2^{int(np.log2(scale))}")
+    for compute in ("f32", "bf16"):
+        got = run_ns(gpu, xs, tdt("f32"), tdt(compute), tdt("f32"), MUON_ABC, 5, EPS)
+        for x, u in zip(xs, got):
+            assert np.isfinite(u).all()
+            e = rel_err(u, oracle.ns_orthogonalize(x, *MUON_ABC, 5, EPS))
+            assert e <= TOL[compute], (compute, x.shape, e)
+
+
 def _workload_inputs(wid):
     ins = [host_matrix(wid, i) for i in range(WORKLOADS[wid].count)]
     return [d["grad"] for d in ins], [d["mom"] for d in ins]
