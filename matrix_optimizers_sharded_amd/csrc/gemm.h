@@ -560,10 +560,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       // Both destinations are k-blocked along their columns (a 128-byte k-block row is
       // one line).  Row-major results (X', or C = A or B') are stored straight from the
       // registers: one instruction writes 64 contiguous bytes of each of 2 rows.  The
-      // transposed copies (X'^T, the mirror tile of C) would leave the registers as 8
-      // or 16 bytes per row per instruction, i.e. 8 partial writes per line, and L2 write
-      // traffic of that shape slows everyone's operand loads.  They go through this
-      // wave's 4 KiB LDS staging slab instead: a round puts 32 columns j x 128 bytes of
+      // mirror tile of C (SYRK and POLY) would leave the registers as 8 or 16 bytes per
+      // row per instruction, i.e. 8 partial writes per line, and L2 write traffic of
+      // that shape slows everyone's operand loads.  It goes through this wave's 4 KiB
+      // LDS staging slab instead: a round puts 32 columns j x 128 bytes of
       // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
       // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
       // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
