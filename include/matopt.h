@@ -180,7 +180,8 @@ int32_t mo_version(void);
  * record a HIP event pair around every kernel they launch (on the call's stream);
  * mo_profile_end() waits for those events and fills up to `max` records, one per
  * kernel kind, returning how many kinds were seen (or a negative code).
- * Profiling state is process-wide; the calls are not thread-safe. */
+ * Profiling state is process-wide and guarded by a lock, so calls from several
+ * threads may interleave; the records then mix every thread's launches. */
 typedef struct {
   char name[32];     /* kernel kind, e.g. "ns_syrk"                               */
   int64_t launches;  /* launches recorded                                          */

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -188,7 +189,10 @@ struct ProfRec {
   int kind;
   hipEvent_t e0, e1;
 };
-bool g_prof = false;
+// Profiling state is shared by every thread that calls the library; g_prof_mu guards
+// the record list and the event pool.
+std::atomic<bool> g_prof{false};
+std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_ev_pool;
 const char* const kKindNames[] = {"momentum_sumsq", "norm_scale", "prep_operand", "scaled_copy",
@@ -197,6 +201,7 @@ const char* const kKindNames[] = {"momentum_sumsq", "norm_scale", "prep_operand"
 enum { PK_MOM = 0, PK_SCALE, PK_PREP, PK_COPY, PK_SYRK, PK_POLY, PK_APPLY, PK_PACK, PK_VOTE, PK_UNPACK,
        PK_SAPPLY, PK_N };
 
+// (g_prof_mu held)
 hipEvent_t take_event() {
   if (!g_ev_pool.empty()) {
     hipEvent_t e = g_ev_pool.back();
@@ -212,16 +217,18 @@ hipEvent_t take_event() {
 template <typename F>
 int launch(int pk, hipStream_t stream, F&& f) {
   ProfRec rec{pk, nullptr, nullptr};
-  if (g_prof) {
+  const bool prof = g_prof.load();
+  if (prof) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     rec.e0 = take_event();
     rec.e1 = take_event();
-    (void)hipEventRecord(rec.e0, stream);
   }
+  if (rec.e0) (void)hipEventRecord(rec.e0, stream);
   f();
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(MO_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
-  if (g_prof) {
-    (void)hipEventRecord(rec.e1, stream);
+  if (rec.e0 && rec.e1 && hipEventRecord(rec.e1, stream) == hipSuccess) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof_recs.push_back(rec);
   }
   return MO_OK;
@@ -236,13 +243,13 @@ int launch(int pk, hipStream_t stream, F&& f) {
 // Blocks of a persistent GEMM launch: one per CU (the LDS ring admits no second
 // block), rounded down to a multiple of the 8 XCDs, never more than the work items.
 int64_t gemm_grid(int64_t total) {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];   // per device, 0 until first asked
   int dev = 0;
   (void)hipGetDevice(&dev);
-  int n = (dev >= 0 && dev < 64) ? cus[dev] : 0;
+  int n = (dev >= 0 && dev < 64) ? cus[dev].load() : 0;
   if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 8;
-    if (dev >= 0 && dev < 64) cus[dev] = n;
+    if (dev >= 0 && dev < 64) cus[dev].store(n);
   }
   const int64_t g = n >= 8 ? n / 8 * 8 : n;
   return std::min<int64_t>(total, g);
@@ -521,6 +528,7 @@ int32_t mo_profile_begin(void) {
 int32_t mo_profile_end(mo_kernel_time* out, int32_t max) {
   g_err.clear();
   g_prof = false;
+  std::lock_guard<std::mutex> lock(g_prof_mu);
   double ms[PK_N] = {0};
   int64_t n[PK_N] = {0};
   int rc = MO_OK;
