@@ -110,6 +110,25 @@ def _stream_ptr(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _one_device(*groups):
+    """The device that every tensor in the given lists (or single tensors) is on;
+    raises if they differ, since the kernels would then get another GPU's pointers."""
+    devs = set()
+    for g in groups:
+        for t in (g if isinstance(g, (list, tuple)) else [g]):
+            if t is not None:
+                devs.add(t.device)
+    if len(devs) != 1:
+        raise MatoptError(-1, f"all tensors must be on one CUDA device, got {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def _on(dev):
+    """Run the enclosed launch with dev current, so the library launches on it."""
+    import torch
+    return torch.cuda.device(dev)
+
+
 def _mats(shapes, grads=None, moms=None, xs=None, outs=None):
     arr = (MoMatrix * max(len(shapes), 1))()
     for i, (r, c) in enumerate(shapes):
@@ -184,13 +203,16 @@ def muon_step_batched(grads, moms, outs, beta, a, b, c, iters, eps=1e-7, compute
     gdt, odt = grads[0].dtype, outs[0].dtype
     if any(g.dtype != gdt for g in grads) or any(o.dtype != odt for o in outs):
         raise MatoptError(-2, "all grads (and all outs) must share one dtype")
+    dev = _one_device(grads, moms, outs)
     mats = _mats(shapes, grads=grads, moms=moms, outs=outs)
     nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
-    ws = (workspace or Workspace(grads[0].device)).get(nbytes)
+    ws = (workspace or Workspace(dev)).get(nbytes)
+    _one_device(grads, ws)
     ns = _ns_params(a, b, c, iters, eps)
-    _check(lib.muon_step_batched(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute), _dtype_code(odt),
-                                 float(beta), ctypes.byref(ns), ws.data_ptr(), ws.numel(),
-                                 _stream_ptr(grads[0])))
+    with _on(dev):
+        _check(lib.muon_step_batched(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute),
+                                     _dtype_code(odt), float(beta), ctypes.byref(ns), ws.data_ptr(),
+                                     ws.numel(), _stream_ptr(grads[0])))
 
 
 def muon_step_apply(grads, moms, weights, beta, a, b, c, iters, lr, eps=1e-7, compute=None,
@@ -213,13 +235,16 @@ def muon_step_apply(grads, moms, weights, beta, a, b, c, iters, lr, eps=1e-7, co
     gdt, wdt = grads[0].dtype, weights[0].dtype
     if any(g.dtype != gdt for g in grads) or any(w.dtype != wdt for w in weights):
         raise MatoptError(-2, "all grads (and all weights) must share one dtype")
+    dev = _one_device(grads, moms, weights)
     mats = _mats(shapes, grads=grads, moms=moms, outs=weights)
     nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
-    ws = (workspace or Workspace(grads[0].device)).get(nbytes)
+    ws = (workspace or Workspace(dev)).get(nbytes)
+    _one_device(grads, ws)
     ns = _ns_params(a, b, c, iters, eps)
-    _check(lib.muon_step_apply(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute), _dtype_code(wdt),
-                               float(beta), ctypes.byref(ns), float(lr), ws.data_ptr(), ws.numel(),
-                               _stream_ptr(grads[0])))
+    with _on(dev):
+        _check(lib.muon_step_apply(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute), _dtype_code(wdt),
+                                   float(beta), ctypes.byref(ns), float(lr), ws.data_ptr(), ws.numel(),
+                                   _stream_ptr(grads[0])))
 
 
 def ns_orthogonalize(xs, outs, a, b, c, iters, eps=1e-7, compute=None, workspace=None):
@@ -239,12 +264,15 @@ def ns_orthogonalize(xs, outs, a, b, c, iters, eps=1e-7, compute=None, workspace
     idt, odt = xs[0].dtype, outs[0].dtype
     if any(x.dtype != idt for x in xs) or any(o.dtype != odt for o in outs):
         raise MatoptError(-2, "all xs (and all outs) must share one dtype")
+    dev = _one_device(xs, outs)
     mats = _mats(shapes, xs=xs, outs=outs)
     nbytes = lib.muon_workspace_bytes(mats, len(shapes), _dtype_code(compute))
-    ws = (workspace or Workspace(xs[0].device)).get(nbytes)
+    ws = (workspace or Workspace(dev)).get(nbytes)
+    _one_device(xs, ws)
     ns = _ns_params(a, b, c, iters, eps)
-    _check(lib.ns_orthogonalize(mats, len(shapes), _dtype_code(idt), _dtype_code(compute), _dtype_code(odt),
-                                ctypes.byref(ns), ws.data_ptr(), ws.numel(), _stream_ptr(xs[0])))
+    with _on(dev):
+        _check(lib.ns_orthogonalize(mats, len(shapes), _dtype_code(idt), _dtype_code(compute), _dtype_code(odt),
+                                    ctypes.byref(ns), ws.data_ptr(), ws.numel(), _stream_ptr(xs[0])))
 
 
 def sign_pack(u, packed=None):
@@ -260,7 +288,8 @@ def sign_pack(u, packed=None):
         packed = torch.empty(nwords, dtype=torch.int32, device=u.device)
     if packed.numel() < nwords or packed.dtype != torch.int32 or not packed.is_contiguous():
         raise MatoptError(-1, "packed must be a contiguous int32 tensor of ceil(numel/32) words")
-    _check(lib.sign_pack(u.data_ptr(), _dtype_code(u.dtype), numel, packed.data_ptr(), _stream_ptr(u)))
+    with _on(_one_device(u, packed)):
+        _check(lib.sign_pack(u.data_ptr(), _dtype_code(u.dtype), numel, packed.data_ptr(), _stream_ptr(u)))
     return packed
 
 
@@ -276,9 +305,12 @@ def sign_vote(packed, numel, out_packed=None, with_sums=False):
         raise MatoptError(-1, "packed width must be ceil(numel/32)")
     if out_packed is None:
         out_packed = torch.empty(nwords, dtype=torch.int32, device=packed.device)
+    if out_packed.dtype != torch.int32 or not out_packed.is_contiguous() or out_packed.numel() < nwords:
+        raise MatoptError(-1, "out_packed must be a contiguous int32 tensor of ceil(numel/32) words")
     sums = torch.empty(numel, dtype=torch.int8, device=packed.device) if with_sums else None
-    _check(lib.sign_vote(packed.data_ptr(), M, numel, out_packed.data_ptr(),
-                         sums.data_ptr() if sums is not None else None, _stream_ptr(packed)))
+    with _on(_one_device(packed, out_packed)):
+        _check(lib.sign_vote(packed.data_ptr(), M, numel, out_packed.data_ptr(),
+                             sums.data_ptr() if sums is not None else None, _stream_ptr(packed)))
     return out_packed, sums
 
 
@@ -300,7 +332,9 @@ def sign_unpack(packed, numel, out=None, dtype=None):
         out = torch.empty(numel, dtype=dtype or torch.bfloat16, device=packed.device)
     if not out.is_cuda or not out.is_contiguous() or out.numel() != numel:
         raise MatoptError(-1, "out must be a contiguous CUDA tensor of numel values")
-    _check(lib.sign_unpack(packed.data_ptr(), numel, _dtype_code(out.dtype), out.data_ptr(), _stream_ptr(packed)))
+    with _on(_one_device(packed, out)):
+        _check(lib.sign_unpack(packed.data_ptr(), numel, _dtype_code(out.dtype), out.data_ptr(),
+                               _stream_ptr(packed)))
     return out
 
 
@@ -311,8 +345,9 @@ def sign_apply(packed, weight, lr):
     _check_packed(packed, numel)
     if not weight.is_cuda or not weight.is_contiguous():
         raise MatoptError(-1, "weight must be a contiguous CUDA tensor")
-    _check(lib.sign_apply(packed.data_ptr(), numel, _dtype_code(weight.dtype), weight.data_ptr(), float(lr),
-                          _stream_ptr(weight)))
+    with _on(_one_device(packed, weight)):
+        _check(lib.sign_apply(packed.data_ptr(), numel, _dtype_code(weight.dtype), weight.data_ptr(), float(lr),
+                              _stream_ptr(weight)))
     return weight
 
 

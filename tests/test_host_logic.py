@@ -172,3 +172,12 @@ def test_product_code_never_imports_the_oracle():
                 if isinstance(sub, (ast.Import, ast.ImportFrom)):
                     mods = [a.name for a in sub.names] if isinstance(sub, ast.Import) else [sub.module or ""]
                     assert not any(m.split(".")[0] == "oracle" for m in mods), node.name
+
+
+def test_binding_rejects_tensors_on_different_devices():
+    import torch
+    from matrix_optimizers_sharded_amd import binding
+    a = torch.zeros(4)
+    assert binding._one_device([a, torch.zeros(2)], a) == torch.device("cpu")
+    with pytest.raises(binding.MatoptError, match="one CUDA device"):
+        binding._one_device([a], torch.zeros(4, device="meta"))
