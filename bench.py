@@ -158,7 +158,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the owner-local step needs "
-              "no collective and this build measures the one GPU's share.", file=sys.stderr)
+              "no collective, so each GPU runs its own owner set and one GPU's rate is measured here.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
