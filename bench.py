@@ -44,12 +44,13 @@ def ns_flops(shapes, iters):
 
 def hbm_bytes(shapes, grad_bytes, compute_bytes, momentum=True):
     """Algorithmic HBM bytes per step of the streaming kernels.
-    momentum_sumsq: read G and M, write M (or read x only); prep_operand: read M,
-    write X in the compute dtype."""
+    momentum_prep (one or more NS iterations): read G and M, write M and the operand X
+    in the compute dtype (or read x, write X); momentum_sumsq (the iters == 0 path):
+    read G and M, write M (or read x only).  The scaled operand rewrite (prep_operand)
+    only runs for norms outside the deferral range, so it has no per-step bytes."""
     numel = sum(r * c for r, c in shapes)
     mom = numel * (grad_bytes + 8) if momentum else numel * grad_bytes
-    src = 4 if momentum else grad_bytes
-    return {"momentum_sumsq": mom, "prep_operand": numel * (src + compute_bytes)}
+    return {"momentum_prep": mom + numel * compute_bytes, "momentum_sumsq": mom}
 
 
 def measure_sign_tail(mo, torch, dev, numel, workers=8, reps=20):

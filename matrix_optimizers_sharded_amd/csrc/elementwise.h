@@ -1,5 +1,6 @@
-// HBM-streaming kernels: the fused momentum + sum-of-squares pass, the per-matrix
-// scale, the scaled/oriented/padded operand writer, and the sign pack / vote.
+// HBM-streaming kernels: the fused momentum + operand pass (and the momentum +
+// sum-of-squares pass of the iters == 0 path), the per-matrix scale, the scaled
+// operand writer for out-of-range norms, and the sign pack / vote.
 #pragma once
 
 #include "common.h"
@@ -91,26 +92,43 @@ __global__ __launch_bounds__(256) void k_momentum_sumsq(const MatDesc* __restric
   if (threadIdx.x == 0) partial[item] = ss;
 }
 
+// Norms inside [2^-20, 2^40] leave the unscaled operand safe for the first products:
+// every |A_ij| <= ||M||_F^2 <= 2^80 accumulates in fp32 without overflow, and the
+// typical element (at least ||M||_F / 2^13 for up to 2^26 elements) squares to well
+// above fp32's smallest normal.
+constexpr double DEFER_NORM_LO = 0x1p-20, DEFER_NORM_HI = 0x1p40;
+
 // One block per matrix: scale = 1 / (sqrt(sum of partials) + eps), summed in fp64
-// in a fixed order.
+// in a fixed order over the matrix's work items of launch kind `kind`.  With
+// `first` (the fused momentum + operand pass wrote X unscaled): first[slot] is the
+// factor the first NS products apply instead (scale, or 1 where the norm lies
+// outside the deferral range), and redo[slot] = 1 marks the matrices whose operand
+// k_prep_redo rewrites scaled.
 __global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ descs,
-                                                    const double* __restrict__ partial,
-                                                    float eps, float* __restrict__ scale) {
+                                                    const double* __restrict__ partial, int kind,
+                                                    float eps, float* __restrict__ scale,
+                                                    float* __restrict__ first, int* __restrict__ redo) {
   const MatDesc& d = descs[blockIdx.x];
   double s = 0.0;
-  const double* p = partial + d.begin[KIND_CHUNK];
-  for (int64_t c = threadIdx.x; c < d.items[KIND_CHUNK]; c += 256) s += p[c];
+  const double* p = partial + d.begin[kind];
+  for (int64_t c = threadIdx.x; c < d.items[kind]; c += 256) s += p[c];
   s = block_sum_256(s);
-  if (threadIdx.x == 0) scale[d.scale_slot] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
+  if (threadIdx.x == 0) {
+    const double norm = sqrt(s);
+    const float sc = static_cast<float>(1.0 / (norm + static_cast<double>(eps)));
+    scale[d.scale_slot] = sc;
+    if (first) {
+      const bool defer = norm >= DEFER_NORM_LO && norm <= DEFER_NORM_HI;
+      first[d.scale_slot] = defer ? sc : 1.f;
+      redo[d.scale_slot] = defer ? 0 : 1;
+    }
+  }
 }
 
-// Pass 2, one 64x64 tile of the padded oriented operand per block: X = S * scale
-// (S = the updated momentum, or the input), written as X (mp x np) in the compute
-// dtype, zero outside the m x n corner.  The source tile is read along its
-// contiguous dimension and X is written along its own, through an LDS tile (the
-// source is the transpose of X when rows > cols).
-// Eight consecutive values stored with 16-byte stores (the address is 16-byte
-// aligned: workspace rows are multiples of 128 bytes and b is a multiple of 8).
+// The operand writers below fill X (mp x np, compute dtype, zero outside the m x n
+// corner) one 64x64 tile per block.  Eight consecutive values go out with 16-byte
+// stores (the address is 16-byte aligned: workspace rows are multiples of 128 bytes
+// and b is a multiple of 8).
 template <typename T>
 __device__ inline void store8(gptr<T> p, const float (&v)[8]);
 template <>
@@ -126,60 +144,16 @@ __device__ inline void store8<float>(gptr<float> p, const float (&v)[8]) {
   reinterpret_cast<gptr<f32x4_t>>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
 }
 
-template <typename TS, typename TC>
-__global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict__ descs, int count,
-                                                      const float* __restrict__ scale,
-                                                      int from_momentum) {
-  __shared__ float tile[PREP_TILE][PREP_TILE + 1];
-  const int64_t item = blockIdx.x;
-  const MatDesc& d = descs[find_desc(descs, count, KIND_PREP, item)];
-  const int64_t local = item - d.begin[KIND_PREP];
-  const int tn = d.np / PREP_TILE;
-  const int i0 = static_cast<int>(local / tn) * PREP_TILE;   // rows of X
-  const int j0 = static_cast<int>(local % tn) * PREP_TILE;   // cols of X
-  const float s = scale[d.scale_slot];
+// Writes X[i0 + a][j0 + b] for a 64 x 64 tile from tile[][] (source orientation):
+// eight consecutive outputs per thread and store, a row piece X[i0 + a][j0 + b ..]
+// (a column piece of the tile when the source is transposed; the padded tile, +1
+// column, keeps those reads free of bank conflicts).  X is k-blocked along its
+// columns, and eight consecutive columns from a multiple of 8 never straddle a
+// k-block.
+template <typename TC>
+__device__ inline void write_operand_tile(const MatDesc& d, int i0, int j0,
+                                          const float (&tile)[PREP_TILE][PREP_TILE + 1]) {
   const int t = threadIdx.x;
-  const int64_t ld = d.cols;
-  // source rows/cols of this tile: X[i][j] = S[i][j] (not transposed) or S[j][i]
-  const int r0 = d.transposed ? j0 : i0, c0 = d.transposed ? i0 : j0;
-  const int64_t rlim = d.rows, clim = d.cols;
-  const float* sm = d.mom;
-  const TS* sx = static_cast<const TS*>(d.grad);
-  if (d.vec_ok && r0 + PREP_TILE <= rlim && c0 + PREP_TILE <= clim) {
-    // whole tile inside the source: four consecutive elements per thread and load
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int a = (t >> 4) + 16 * q, b = (t & 15) * 4;
-      const int64_t e = (r0 + a) * ld + c0 + b;
-      float v[4];
-      if (from_momentum) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(sm + e);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = x[k];
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = static_cast<float>(sx[e + k]);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) tile[a][b + k] = v[k] * s;
-    }
-  } else {
-    const int tx = t & 63, ty = t >> 6;
-#pragma unroll 4
-    for (int q = 0; q < 16; ++q) {
-      const int a = ty + 4 * q;
-      const int64_t r = r0 + a, c = c0 + tx;
-      float v = 0.f;
-      if (r < rlim && c < clim) v = from_momentum ? sm[r * ld + c] : static_cast<float>(sx[r * ld + c]);
-      tile[a][tx] = v * s;
-    }
-  }
-  __syncthreads();
-  // eight consecutive outputs per thread and store: a row piece X[i0 + a][j0 + b ..]
-  // (a column piece of the tile when the source is transposed; the padded tile, +1
-  // column, keeps those reads free of bank conflicts).  X is k-blocked along its
-  // columns, and eight consecutive columns from a multiple of 8 never straddle a
-  // k-block.
   unsigned char* const X = static_cast<unsigned char*>(d.X[0]);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -188,6 +162,150 @@ __global__ __launch_bounds__(256) void k_prep_operand(const MatDesc* __restrict_
 #pragma unroll
     for (int k = 0; k < 8; ++k) vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];
     store8<TC>(global(reinterpret_cast<TC*>(X + kb_off<TC>(i0 + a, j0 + b, d.pX))), vx);
+  }
+}
+
+// The fused first pass of a step with at least one NS iteration, MP_TPB consecutive
+// 64x64 tiles of one row of the padded oriented operand per block (256 threads;
+// items per matrix are a multiple of 16 and tiles per operand row of 4, so a
+// block's tiles never cross a row or a matrix): with MOMENTUM, M <- fma(beta, M, G)
+// in place over the tiles' source elements; X = M (or the input), unscaled, in the
+// compute dtype, zero outside the m x n corner; and the block's fp64 sum of squares
+// to partial[first item] (0 to the others).  One HBM sweep: G and M read once, M
+// and X written once.  The Frobenius scale s comes afterwards, applied by the first
+// NS products (s^2 on X X^T, s on the first B X), which in exact arithmetic is the
+// same as scaling X first: (sX)(sX)^T = s^2 X X^T and B'(sX) = s B'X.
+// Four tiles per block (2 blocks per CU by LDS) measured fastest: 5.1-5.7 TB/s
+// against 4.7-5.3 TB/s with one tile per block at the 7B-class owner set, as more
+// of each thread's loads are in flight before its first store.
+#ifndef MO_MP_TPB
+#define MO_MP_TPB 4
+#endif
+constexpr int MP_TPB = MO_MP_TPB;
+static_assert(MP_TPB == 1 || MP_TPB == 2 || MP_TPB == 4, "tiles per block: 1, 2 or 4");
+template <typename TG, typename TC, bool MOMENTUM>
+__global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict__ descs, int count,
+                                                       float beta, double* __restrict__ partial) {
+  __shared__ float tile[MP_TPB][PREP_TILE][PREP_TILE + 1];
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * MP_TPB;
+  const MatDesc& d = descs[find_desc(descs, count, KIND_PREP, item)];
+  const int64_t local = item - d.begin[KIND_PREP];
+  const int tn = d.np / PREP_TILE;
+  const int i0 = static_cast<int>(local / tn) * PREP_TILE;    // rows of X
+  const int jb = static_cast<int>(local % tn) * PREP_TILE;    // first column of X; tile u at jb + 64u
+  const int t = threadIdx.x;
+  const int64_t ld = d.cols;
+  const int64_t rlim = d.rows, clim = d.cols;
+  const TG* __restrict__ g = static_cast<const TG*>(d.grad);
+  float* __restrict__ m = d.mom;
+  // source rows/cols of tile u: X[i][j] = S[i][j] (not transposed) or S[j][i]
+  auto src_r0 = [&](int u) { return d.transposed ? jb + PREP_TILE * u : i0; };
+  auto src_c0 = [&](int u) { return d.transposed ? i0 : jb + PREP_TILE * u; };
+  bool inside = d.vec_ok;
+#pragma unroll
+  for (int u = 0; u < MP_TPB; ++u)
+    inside = inside && src_r0(u) + PREP_TILE <= rlim && src_c0(u) + PREP_TILE <= clim;
+  double ss = 0.0;
+  if (inside) {
+    // whole tiles inside the source: four consecutive elements per thread and load,
+    // all loads of the thread issued before the first store
+    f32x4_t gv[MP_TPB][4], mv[MP_TPB][4];
+#pragma unroll
+    for (int u = 0; u < MP_TPB; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = (t >> 4) + 16 * q, b = (t & 15) * 4;
+        const int64_t e = (src_r0(u) + a) * ld + src_c0(u) + b;
+        gv[u][q] = load4_f32<TG>(g + e);
+        if (MOMENTUM) mv[u][q] = *reinterpret_cast<const f32x4_t*>(m + e);
+      }
+#pragma unroll
+    for (int u = 0; u < MP_TPB; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = (t >> 4) + 16 * q, b = (t & 15) * 4;
+        f32x4_t v = gv[u][q];
+        if (MOMENTUM) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(beta, mv[u][q][k], gv[u][q][k]);
+          *reinterpret_cast<f32x4_t*>(m + (src_r0(u) + a) * ld + src_c0(u) + b) = v;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ss = __builtin_fma(static_cast<double>(v[k]), static_cast<double>(v[k]), ss);
+          tile[u][a][b + k] = v[k];
+        }
+      }
+  } else {
+    const int tx = t & 63, ty = t >> 6;
+    for (int u = 0; u < MP_TPB; ++u) {
+      const int r0 = src_r0(u), c0 = src_c0(u);
+#pragma unroll 4
+      for (int q = 0; q < 16; ++q) {
+        const int a = ty + 4 * q;
+        const int64_t r = r0 + a, c = c0 + tx;
+        float v = 0.f;
+        if (r < rlim && c < clim) {
+          v = static_cast<float>(g[r * ld + c]);
+          if (MOMENTUM) {
+            v = __builtin_fmaf(beta, m[r * ld + c], v);
+            m[r * ld + c] = v;
+          }
+        }
+        ss = __builtin_fma(static_cast<double>(v), static_cast<double>(v), ss);
+        tile[u][a][tx] = v;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < MP_TPB; ++u) write_operand_tile<TC>(d, i0, jb + PREP_TILE * u, tile[u]);
+  ss = block_sum_256(ss);
+  if (t < MP_TPB) partial[item + t] = t == 0 ? ss : 0.0;
+}
+
+// X = S * scale for the matrices flagged in redo[] (their norm lies outside the range
+// where the first products may take the scale, see k_norm_scale): S is the updated
+// momentum or the input, X the padded oriented operand in the compute dtype.  The
+// grid strides over each flagged matrix's 64x64 tiles; a block first checks 256
+// flags at a time, so with nothing flagged the launch costs a few microseconds.  The
+// source tile is read along its contiguous dimension and X is written along its own,
+// through an LDS tile (the source is the transpose of X when rows > cols).
+template <typename TS, typename TC>
+__global__ __launch_bounds__(256) void k_prep_redo(const MatDesc* __restrict__ descs, int count,
+                                                   const float* __restrict__ scale,
+                                                   const int* __restrict__ redo, int from_momentum) {
+  __shared__ float tile[PREP_TILE][PREP_TILE + 1];
+  const int t = threadIdx.x;
+  for (int c0 = 0; c0 < count; c0 += 256) {
+    const int c = c0 + t;
+    if (!__syncthreads_or(c < count && redo[descs[c].scale_slot])) continue;
+    const int c1 = c0 + 256 < count ? c0 + 256 : count;
+    for (int k = c0; k < c1; ++k) {
+      const MatDesc& d = descs[k];
+      if (!redo[d.scale_slot]) continue;
+      const float s = scale[d.scale_slot];
+      const int tn = d.np / PREP_TILE;
+      const int64_t ld = d.cols, rlim = d.rows, clim = d.cols;
+      const float* sm = d.mom;
+      const TS* sx = static_cast<const TS*>(d.grad);
+      for (int64_t local = blockIdx.x; local < d.items[KIND_PREP]; local += gridDim.x) {
+        const int i0 = static_cast<int>(local / tn) * PREP_TILE;
+        const int j0 = static_cast<int>(local % tn) * PREP_TILE;
+        const int r0 = d.transposed ? j0 : i0, cc0 = d.transposed ? i0 : j0;
+        const int tx = t & 63, ty = t >> 6;
+        for (int q = 0; q < 16; ++q) {
+          const int a = ty + 4 * q;
+          const int64_t r = r0 + a, cc = cc0 + tx;
+          float v = 0.f;
+          if (r < rlim && cc < clim) v = from_momentum ? sm[r * ld + cc] : static_cast<float>(sx[r * ld + cc]);
+          tile[a][tx] = v * s;
+        }
+        __syncthreads();
+        write_operand_tile<TC>(d, i0, j0, tile);
+        __syncthreads();   // the next tile overwrites tile[][]
+      }
+    }
   }
 }
 

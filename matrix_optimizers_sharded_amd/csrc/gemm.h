@@ -280,7 +280,7 @@ struct TileRef {
 template <typename T, int MODE, typename TO>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
 void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int parity, float ca, float cb,
-               float cc) {
+               float cc, const float* __restrict__ first) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[GEMM_LDS_BYTES];
   // per-wave 4 KiB epilogue staging slabs
   __shared__ __attribute__((aligned(16))) unsigned char staging[NWAVES * 4096];
@@ -553,6 +553,15 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       const MatDesc& d = descs[__builtin_amdgcn_readfirstlane(cur.di)];
       const int ti = cur.ti, tj = cur.tj;
       const int i0 = ti * GT, j0 = tj * GT;
+      // The first iteration's operand X is the unscaled momentum when `first` is
+      // given: SYRK then scales its products by f^2 and APPLY by f, the matrix's
+      // Frobenius factor (f = 1 where X was written scaled).  Otherwise alpha = 1,
+      // and acc * 1 is acc exactly.
+      float alpha = 1.f;
+      if (MODE != GM_POLY && first != nullptr) {
+        const float f = first[d.scale_slot];
+        alpha = MODE == GM_SYRK ? f * f : f;
+      }
       // Epilogue.  Accumulator layout of a 32x32 MFMA block: lane l, register r holds
       // row 8*(r/4) + 4*(l/32) + r%4, column l%32, so each lane owns 4 consecutive rows
       // ib..ib+3 of one column j per register group g.
@@ -592,7 +601,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         auto values = [&](int a, int b, int g, int ib, int j, const v4_t& e, float (&v)[4]) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            v[t] = acc[a][b][4 * g + t];
+            v[t] = acc[a][b][4 * g + t] * alpha;
             if (MODE == GM_POLY) {
               v[t] = cb * to_f32(e[t]) + cc * v[t];
               if (diag && ib + t == j && j < d.m) v[t] += ca;
@@ -673,7 +682,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
               const int j = j0 + wn + b * 32 + l32;
               float v[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t];
+              for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t] * alpha;
               // the value stored at o: U itself, or W - lr * U
               auto result = [&](gptr<TO> o, float u) {
                 return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);

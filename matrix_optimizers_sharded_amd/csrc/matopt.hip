@@ -3,11 +3,15 @@
 // One batched call = one descriptor table (uploaded to the head of the caller's
 // workspace through a pinned staging ring) + a fixed launch sequence on the
 // caller's stream:
-//   k_momentum_sumsq   momentum fma in place + per-chunk sum of squares  (HBM)
-//   k_norm_scale       per-matrix 1 / (||M||_F + eps)                    (tiny)
-//   k_prep_operand     scaled, oriented, zero-padded X0 and X0^T         (HBM)
+//   k_momentum_prep    momentum fma in place, the unscaled oriented operand X,
+//                      per-tile sum of squares                          (HBM)
+//   k_norm_scale       per-matrix s = 1 / (||M||_F + eps)                (tiny)
+//   k_prep_redo        X = s M for norms outside the deferral range     (usually idle)
 //   iters x { k_ns_gemm<SYRK>, k_ns_gemm<POLY>, k_ns_gemm<APPLY> }       (MFMA)
 //             A = X X^T,  B' = aI + bA + cA^2,  X <- B' X
+//             (the first SYRK and APPLY take the factor s^2 and s)
+// With iters == 0 the sequence is k_momentum_sumsq (momentum + per-chunk sum of
+// squares), k_norm_scale and k_scaled_copy (U = s M).
 // Each launch covers every matrix of the batch (grouped launch); blocks find their
 // matrix by binary search over the table, which is sorted by decreasing size so
 // the longest tiles start first.  The GEMM launches are persistent: one block per
@@ -22,6 +26,7 @@
 #include <mutex>
 #include <numeric>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/matopt.h"
@@ -55,6 +60,8 @@ struct Plan {
   int64_t total[NKIND] = {0, 0, 0, 0, 0};
   size_t off_desc = 0, off_scale = 0, off_partial = 0, bytes = 0;
 };
+// The per-matrix scalars at off_scale: scale[count] (s = 1 / (||M||_F + eps)),
+// first[count] (the factor the first NS products apply) and redo[count] (int flags).
 
 // Validate the list and lay out the workspace.  base == nullptr only sizes it.
 int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, unsigned char* base,
@@ -85,11 +92,17 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
   plan.off_desc = off;
   off = align_up(off + sizeof(MatDesc) * std::max(count, 1), ALIGN);
   plan.off_scale = off;
-  off = align_up(off + sizeof(float) * std::max(count, 1), ALIGN);
-  int64_t chunks = 0;
-  for (int i = 0; i < count; ++i) chunks += (mats[i].rows * mats[i].cols + CHUNK - 1) / CHUNK;
+  off = align_up(off + (2 * sizeof(float) + sizeof(int)) * std::max(count, 1), ALIGN);
+  // one fp64 partial sum per 4096-element chunk (iters == 0) or per 64x64 operand
+  // tile (the fused pass)
+  int64_t chunks = 0, tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t r = mats[i].rows, c = mats[i].cols;
+    chunks += (r * c + CHUNK - 1) / CHUNK;
+    tiles += (round_up(std::min(r, c), GEMM_TILE) / PREP_TILE) * (round_up(std::max(r, c), GEMM_TILE) / PREP_TILE);
+  }
   plan.off_partial = off;
-  off = align_up(off + sizeof(double) * std::max<int64_t>(chunks, 1), ALIGN);
+  off = align_up(off + sizeof(double) * std::max<int64_t>(std::max(chunks, tiles), 1), ALIGN);
 
   plan.descs.resize(count);
   for (int k = 0; k < count; ++k) {
@@ -195,11 +208,11 @@ std::atomic<bool> g_prof{false};
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_ev_pool;
-const char* const kKindNames[] = {"momentum_sumsq", "norm_scale", "prep_operand", "scaled_copy",
-                                  "ns_syrk",        "ns_poly",    "ns_apply",     "sign_pack",
-                                  "sign_vote",      "sign_unpack", "sign_apply"};
+const char* const kKindNames[] = {"momentum_sumsq", "norm_scale",  "prep_operand", "scaled_copy",
+                                  "ns_syrk",        "ns_poly",     "ns_apply",     "sign_pack",
+                                  "sign_vote",      "sign_unpack", "sign_apply",   "momentum_prep"};
 enum { PK_MOM = 0, PK_SCALE, PK_PREP, PK_COPY, PK_SYRK, PK_POLY, PK_APPLY, PK_PACK, PK_VOTE, PK_UNPACK,
-       PK_SAPPLY, PK_N };
+       PK_SAPPLY, PK_MOMPREP, PK_N };
 
 // (g_prof_mu held)
 hipEvent_t take_event() {
@@ -264,61 +277,105 @@ struct ApplyOpt {
 
 template <typename T, typename TO>
 int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
-           hipStream_t stream) {
+           const float* first, hipStream_t stream) {
   const int64_t gs = gemm_grid(plan.total[KIND_SYRK]), ga = gemm_grid(plan.total[KIND_APPLY]);
   for (int t = 0; t < ns.iters; ++t) {
     const int parity = t & 1;
+    const float* f = t == 0 ? first : nullptr;   // the Frobenius factor, first iteration only
     MO_TRY(launch(PK_SYRK, stream, [&] {
       hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                         dd, count, plan.total[KIND_SYRK], parity, 0.f, 0.f, 0.f);
+                         dd, count, plan.total[KIND_SYRK], parity, 0.f, 0.f, 0.f, f);
     }));
     MO_TRY(launch(PK_POLY, stream, [&] {
       hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                         dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c);
+                         dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c, nullptr);
     }));
     const bool last = (t + 1 == ns.iters);
     MO_TRY(launch(PK_APPLY, stream, [&] {
       if (last && ap.on)
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, ap.lr, 0.f, 0.f);
+                           dd, count, plan.total[KIND_APPLY], parity, ap.lr, 0.f, 0.f, f);
       else if (last)
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f);
+                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f, f);
       else
         hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f);
+                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f, f);
     }));
   }
   return MO_OK;
 }
 
-template <typename TS, typename TC, typename TO>
-int run_after_scale(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
-                    const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
+// Per-matrix device scalars and partial sums inside the workspace.
+struct Scalars {
+  float* scale;
+  float* first;
+  int* redo;
+  double* partial;
+};
+
+// The launch sequence after the descriptor upload.  TG: the dtype of the input
+// (gradient, or x for orthogonalise only); TC: compute; TO: output.
+template <typename TG, typename TC, typename TO>
+int run_step(const MatDesc* dd, int count, const Plan& plan, const Scalars& sc, bool momentum, float beta,
+             const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
+  // the NS source after the first pass: the fp32 momentum, or the input itself
+  typedef typename std::conditional<std::is_same<TG, float>::value, float, bf16_t>::type TX;
   const int from_mom = momentum ? 1 : 0;
   if (ns.iters == 0) {
+    MO_TRY(launch(PK_MOM, stream, [&] {
+      const dim3 grid(plan.total[KIND_CHUNK]);
+      if (momentum)
+        hipLaunchKernelGGL((k_momentum_sumsq<TG, true>), grid, dim3(256), 0, stream, dd, count, beta, sc.partial);
+      else
+        hipLaunchKernelGGL((k_momentum_sumsq<TG, false>), grid, dim3(256), 0, stream, dd, count, beta, sc.partial);
+    }));
+    MO_TRY(launch(PK_SCALE, stream, [&] {
+      hipLaunchKernelGGL(k_norm_scale, dim3(count), dim3(256), 0, stream, dd, sc.partial, int(KIND_CHUNK), ns.eps,
+                         sc.scale, static_cast<float*>(nullptr), static_cast<int*>(nullptr));
+    }));
     return launch(PK_COPY, stream, [&] {
-      hipLaunchKernelGGL((k_scaled_copy<TS, TO>), dim3(plan.total[KIND_CHUNK]), dim3(256), 0, stream, dd,
-                         count, scale, from_mom, ap.on ? 1 : 0, ap.lr);
+      if (momentum)
+        hipLaunchKernelGGL((k_scaled_copy<float, TO>), dim3(plan.total[KIND_CHUNK]), dim3(256), 0, stream, dd,
+                           count, sc.scale, from_mom, ap.on ? 1 : 0, ap.lr);
+      else
+        hipLaunchKernelGGL((k_scaled_copy<TX, TO>), dim3(plan.total[KIND_CHUNK]), dim3(256), 0, stream, dd,
+                           count, sc.scale, from_mom, ap.on ? 1 : 0, ap.lr);
     });
   }
-  MO_TRY(launch(PK_PREP, stream, [&] {
-    hipLaunchKernelGGL((k_prep_operand<TS, TC>), dim3(plan.total[KIND_PREP]), dim3(256), 0, stream, dd,
-                       count, scale, from_mom);
+  MO_TRY(launch(PK_MOMPREP, stream, [&] {
+    const dim3 grid(plan.total[KIND_PREP] / MP_TPB);   // a multiple of 16 items per matrix
+    if (momentum)
+      hipLaunchKernelGGL((k_momentum_prep<TG, TC, true>), grid, dim3(256), 0, stream, dd, count, beta, sc.partial);
+    else
+      hipLaunchKernelGGL((k_momentum_prep<TG, TC, false>), grid, dim3(256), 0, stream, dd, count, beta, sc.partial);
   }));
-  return run_ns<TC, TO>(dd, count, plan, ns, ap, stream);
+  MO_TRY(launch(PK_SCALE, stream, [&] {
+    hipLaunchKernelGGL(k_norm_scale, dim3(count), dim3(256), 0, stream, dd, sc.partial, int(KIND_PREP), ns.eps,
+                       sc.scale, sc.first, sc.redo);
+  }));
+  MO_TRY(launch(PK_PREP, stream, [&] {
+    const dim3 grid(std::min<int64_t>(plan.total[KIND_PREP], 2048));
+    if (momentum)
+      hipLaunchKernelGGL((k_prep_redo<float, TC>), grid, dim3(256), 0, stream, dd, count, sc.scale, sc.redo,
+                         from_mom);
+    else
+      hipLaunchKernelGGL((k_prep_redo<TX, TC>), grid, dim3(256), 0, stream, dd, count, sc.scale, sc.redo,
+                         from_mom);
+  }));
+  return run_ns<TC, TO>(dd, count, plan, ns, ap, sc.first, stream);
 }
 
-template <typename TS>
-int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const float* scale, bool momentum,
-                         int compute, int out, const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
+template <typename TG>
+int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const Scalars& sc, bool momentum,
+                         float beta, int compute, int out, const mo_ns_params& ns, const ApplyOpt& ap,
+                         hipStream_t stream) {
   if (compute == MO_BF16) {
-    if (out == MO_BF16)
-      return run_after_scale<TS, bf16_t, bf16_t>(dd, count, plan, scale, momentum, ns, ap, stream);
-    return run_after_scale<TS, bf16_t, float>(dd, count, plan, scale, momentum, ns, ap, stream);
+    if (out == MO_BF16) return run_step<TG, bf16_t, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
+    return run_step<TG, bf16_t, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
   }
-  if (out == MO_BF16) return run_after_scale<TS, float, bf16_t>(dd, count, plan, scale, momentum, ns, ap, stream);
-  return run_after_scale<TS, float, float>(dd, count, plan, scale, momentum, ns, ap, stream);
+  if (out == MO_BF16) return run_step<TG, float, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
+  return run_step<TG, float, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
 }
 
 int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out, bool momentum, float beta,
@@ -346,31 +403,15 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   MO_TRY(build_plan(mats, count, compute, momentum, base, full, in_dtype, out));
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   MatDesc* dd = reinterpret_cast<MatDesc*>(base + full.off_desc);
-  float* scale = reinterpret_cast<float*>(base + full.off_scale);
-  double* partial = reinterpret_cast<double*>(base + full.off_partial);
+  Scalars sc;
+  sc.scale = reinterpret_cast<float*>(base + full.off_scale);
+  sc.first = sc.scale + count;
+  sc.redo = reinterpret_cast<int*>(sc.first + count);
+  sc.partial = reinterpret_cast<double*>(base + full.off_partial);
   MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
-
-  MO_TRY(launch(PK_MOM, stream, [&] {
-    const dim3 grid(full.total[KIND_CHUNK]);
-    if (momentum) {
-      if (in_dtype == MO_BF16)
-        hipLaunchKernelGGL((k_momentum_sumsq<bf16_t, true>), grid, dim3(256), 0, stream, dd, count, beta, partial);
-      else
-        hipLaunchKernelGGL((k_momentum_sumsq<float, true>), grid, dim3(256), 0, stream, dd, count, beta, partial);
-    } else {
-      if (in_dtype == MO_BF16)
-        hipLaunchKernelGGL((k_momentum_sumsq<bf16_t, false>), grid, dim3(256), 0, stream, dd, count, beta, partial);
-      else
-        hipLaunchKernelGGL((k_momentum_sumsq<float, false>), grid, dim3(256), 0, stream, dd, count, beta, partial);
-    }
-  }));
-  MO_TRY(launch(PK_SCALE, stream, [&] {
-    hipLaunchKernelGGL(k_norm_scale, dim3(count), dim3(256), 0, stream, dd, partial, ns->eps, scale);
-  }));
-  // after the momentum step the NS source is the fp32 momentum; otherwise the input
-  if (momentum || in_dtype == MO_F32)
-    return dispatch_compute_out<float>(dd, count, full, scale, momentum, compute, out, *ns, ap, stream);
-  return dispatch_compute_out<bf16_t>(dd, count, full, scale, momentum, compute, out, *ns, ap, stream);
+  if (in_dtype == MO_BF16)
+    return dispatch_compute_out<bf16_t>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
+  return dispatch_compute_out<float>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
 }
 
 }  // namespace

@@ -29,7 +29,8 @@ KINDS = [
     (re.compile(r"k_ns_gemm.*Li1E"), "ns_poly"),
     (re.compile(r"k_ns_gemm.*Li[234]E"), "ns_apply"),
     (re.compile(r"k_momentum_sumsq"), "momentum_sumsq"),
-    (re.compile(r"k_prep_operand"), "prep_operand"),
+    (re.compile(r"k_momentum_prep"), "momentum_prep"),
+    (re.compile(r"k_prep_redo"), "prep_operand"),
     (re.compile(r"k_norm_scale"), "norm_scale"),
     (re.compile(r"k_scaled_copy"), "scaled_copy"),
     (re.compile(r"k_sign_pack"), "sign_pack"),

@@ -212,6 +212,32 @@ def test_extreme_input_scales(gpu, scale):
             assert e <= TOL[compute], (compute, x.shape, e)
 
 
+def test_first_product_scaling_range(gpu):
+    """The first pass writes the operand unscaled and the first products apply the
+    Frobenius factor, unless the norm lies outside [2^-20, 2^40]; then the operand is
+    rewritten scaled.  One batch holds matrices just inside and just outside both
+    ends (norms about 2^-19.4, 2^-21.4, 2^39.6, 2^40.6), so both routes run side by
+    side in one call and each must follow the oracle."""
+    import torch
+    shapes = [(300, 520), (520, 300), (300, 520), (520, 300)]
+    exps = [-28, -30, 31, 32]   # the unit Gaussians have norm about 2^8.6
+    xs = [(gaussian(s, 720 + i) * np.float32(2.0 ** e)).astype(np.float32) for i, (s, e) in enumerate(zip(shapes, exps))]
+    norms = [np.log2(np.linalg.norm(x.astype(np.float64))) for x in xs]
+    assert norms[0] > -20 > norms[1] and norms[2] < 40 < norms[3], norms
+    say(f"first-product scaling, log2 norms {[round(v, 2) for v in norms]}")
+    for compute in ("f32", "bf16"):
+        got = run_ns(gpu, xs, tdt("f32"), tdt(compute), tdt("f32"), MUON_ABC, 5, EPS)
+        for x, u in zip(xs, got):
+            e = rel_err(u, oracle.ns_orthogonalize(x, *MUON_ABC, 5, EPS))
+            assert e <= TOL[compute], (compute, x.shape, e)
+    # the momentum step too: G = x, M = 0 makes the new momentum x itself
+    zeros = [np.zeros_like(x) for x in xs]
+    for compute in (torch.float32, torch.bfloat16):
+        gm, gu = run_muon(gpu, xs, zeros, torch.float32, compute, torch.float32, BETA, MUON_ABC, 5, EPS)
+        check_muon(xs, zeros, gm, gu, "f32" if compute == torch.float32 else "bf16", MUON_ABC, 5,
+                   label="first-product scaling")
+
+
 def _workload_inputs(wid):
     ins = [host_matrix(wid, i) for i in range(WORKLOADS[wid].count)]
     return [d["grad"] for d in ins], [d["mom"] for d in ins]

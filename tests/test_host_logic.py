@@ -70,7 +70,7 @@ def test_bench_flop_accounting_matches_oracle_formula():
     assert abs(total - 4.7485e14) / 4.7485e14 < 1e-3
     b = bench.hbm_bytes(shapes, 2, 2)
     assert b["momentum_sumsq"] == W.WORKLOADS[4].numel * 10
-    assert b["prep_operand"] == W.WORKLOADS[4].numel * 6   # read fp32 M, write bf16 X
+    assert b["momentum_prep"] == W.WORKLOADS[4].numel * 12   # + write bf16 X
 
 
 def test_profsummary_round_trip(tmp_path):
