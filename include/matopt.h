@@ -98,6 +98,11 @@ size_t muon_workspace_bytes(const mo_matrix *mats, int32_t count, int32_t comput
  * (bf16 operands X, A, B with fp32 accumulation; A is rounded to bf16 once, and the
  * polynomial matrix a*I + b*A + c*A^2 is formed from that same rounded A and rounded
  * to bf16 once, so that each step is the single product X <- (a*I + b*A + c*A^2) X).
+ * The scale s = 1 / (||M||_F + eps) enters through the first iteration's products
+ * (s^2 on X X^T, s on the update), with the first X being M itself in the compute
+ * dtype: the same in exact arithmetic, one HBM pass fewer.  Where ||M||_F lies
+ * outside [2^-20, 2^40], X is scaled before the first product instead, so fp32
+ * accumulation never overflows or underflows.
  * out_dtype: MO_F32 or MO_BF16.
  * out must not overlap grad or momentum.  Deterministic: identical inputs give
  * bit-identical outputs, and a matrix's result does not depend on the rest of
