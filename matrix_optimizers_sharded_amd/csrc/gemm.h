@@ -310,6 +310,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // one column per lane, comes out of transposing reads.  Wave w's load q covers 8
   // rows of k-block (NWAVES q + w) / RG, from row ((NWAVES q + w) % RG) * 8.
   constexpr bool QT = MODE == GM_APPLY || MODE == GM_APPLY_FINAL || MODE == GM_APPLY_WEIGHT;
+  constexpr bool EARLY_P = MODE == GM_POLY;   // POLY: P loads before the last step's MFMAs
   constexpr int KB = ROW_BYTES / static_cast<int>(sizeof(T));   // elements per k-block
   constexpr int KR = KB;                                         // k rows per slab
   constexpr int JB = GT / KB;                                    // k-blocks per tile width
@@ -365,22 +366,23 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
     }
   };
   static_assert(INST_PER_OPERAND % 4 == 0, "loads per operand per wave: a multiple of 4");
-  auto issue = [&](const TileRef& t, int kt, int stage) {
-    const uint32_t sp = kt * t.kP, sq = kt * t.kQ;   // k-block kt of P and of Q
-    const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024;
+  // this wave's loads of k-block kt of one operand (h = 0: P, h = 1: Q) into a stage
+  auto issue_op = [&](const TileRef& t, int kt, int stage, int h) {
+    const uint32_t base = lds_addr(smem) + stage * STAGE_BYTES + wave * 1024 + (h ? OPERAND_BYTES : 0);
 #pragma unroll
     for (int q0 = 0; q0 < INST_PER_OPERAND; q0 += 4) {
-      uint32_t lp[4], lq[4], vp[4], vq[4];
+      uint32_t l[4], vo[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        lp[q] = base + (q0 + q) * NWAVES * 1024;
-        lq[q] = lp[q] + OPERAND_BYTES;
-        vp[q] = t.vP0 + (q0 + q) * VSTEP;
-        vq[q] = t.vQ0 + (q0 + q) * t.qQ;
+        l[q] = base + (q0 + q) * NWAVES * 1024;
+        vo[q] = h ? t.vQ0 + (q0 + q) * t.qQ : t.vP0 + (q0 + q) * VSTEP;
       }
-      load_lds16x4(t.rP, lp, vp, sp);
-      load_lds16x4(t.rQ, lq, vq, sq);
+      load_lds16x4(h ? t.rQ : t.rP, l, vo, kt * (h ? t.kQ : t.kP));
     }
+  };
+  auto issue = [&](const TileRef& t, int kt, int stage) {
+    issue_op(t, kt, stage, 0);
+    issue_op(t, kt, stage, 1);
   };
 
   f32x16_t acc[4][NB];
@@ -405,9 +407,15 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // k16 steps: steps 0..KSTEPS-2 read the next step's fragments, then run 8 MFMAs;
   // then wait until this wave's loads of slab kt+1 have landed (later slabs may stay
   // in flight) and its own LDS reads are done, one barrier (slab kt+1 is in LDS for
-  // everyone, and nobody reads slab kt any more), start the loads of slab
-  // kt+NSTAGE (of this tile or the next) into slab kt's stage, read slab kt+1's
-  // first fragments; the last step's 8 MFMAs hide that barrier and those reads.
+  // everyone, and nobody reads slab kt any more), read slab kt+1's first fragments
+  // beside the last step's 8 MFMAs, and only then start the loads of slab kt+NSTAGE
+  // (of this tile or the next) into slab kt's stage.  Right after the barrier all
+  // eight waves would otherwise issue their 64 direct-to-LDS loads at once: the
+  // texture-address command FIFO fills (rocprofv3 SQ_VMEM_TA_CMD_FIFO_FULL), waves
+  // stall at issue, and their MFMAs wait behind the loads.  With the MFMAs issued
+  // first the matrix cores stay busy while the loads drain.  Measured against loads
+  // first, on two boxes: APPLY and SYRK -5%; POLY -1% with all loads after, -4% with
+  // its P loads before and Q loads after the MFMAs (EARLY_P).
   // The waits count loads only: buffer loads complete in issue order, so "at most
   // n outstanding", with n the loads issued after slab kt+1's, means slab kt+1 is
   // in, whatever stores or atomics are also in flight.
@@ -533,17 +541,23 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       // below fetch stale, unused fragments.
       wait_loads(has_next ? NSTAGE - 2 : min(NSTAGE - 2, cur.nk - kt - 2));
       __syncthreads();
-      // one issue site for both cases (see load_lds16x4)
-      {
-        const int ks = kt + NSTAGE;
-        const bool own = ks < cur.nk;
-        if (own || has_next) issue(own ? cur : nxt, own ? ks : ks - cur.nk, stage);
-      }
+      // slab kt + NSTAGE (of this tile or the next) goes into slab kt's stage; one
+      // issue site per operand for both cases (see load_lds16x4)
+      const int ks = kt + NSTAGE;
+      const bool own = ks < cur.nk;
+      const bool load = own || has_next;
+      const TileRef& lt = own ? cur : nxt;
+      const int lk = own ? ks : ks - cur.nk;
+      if (EARLY_P && load) issue_op(lt, lk, stage, 0);
       read_frags(smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
       MO_STEP_FENCE();
       mfma_step(fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
       MO_STEP_INTERLEAVE();
       __builtin_amdgcn_sched_barrier(0);
+      if (load) {
+        if (!EARLY_P) issue_op(lt, lk, stage, 0);
+        issue_op(lt, lk, stage, 1);
+      }
       stage = next;
     }
 
