@@ -1,16 +1,17 @@
 // The three Newton-Schulz products as one MFMA GEMM core with three epilogues.
 //
-// Every product is C[i][j] = sum_k P[i][k] * Q[j][k] with both operands read along
-// k-contiguous rows:
-//   SYRK   A  = X X^T         P = Q = X (rows of X, k over n); upper tiles only,
-//                             each off-diagonal tile also stored mirrored
+// Every product is C[i][j] = sum_k P[i][k] * Q(k, j), P read along k-contiguous rows:
+//   SYRK   A  = X X^T         P = Q = X (rows of X, k over n), Q(k, j) = X[j][k];
+//                             upper tiles only, each off-diagonal tile also
+//                             stored mirrored
 //   POLY   B' = aI + bA + c A A   P = Q = A (A symmetric, so A A = A A^T); upper
 //                             tiles, mirrored; b*A in the epilogue reads the same
 //                             rounded A, and a is added on the diagonal (rows < m)
-//   APPLY  X' = B' X = aX + (bA + cA^2) X   P = B', Q = X^T (the kernel keeps X^T
-//                             as a second copy so this is k-contiguous too); the
-//                             epilogue only stores: X' in place and X'^T to the
-//                             other ping-pong buffer, or the final U to the caller.
+//   APPLY  X' = B' X = aX + (bA + cA^2) X   P = B', Q(k, j) = X[k][j]: X itself,
+//                             whose slab (rows k, the tile's columns j) gfx950's
+//                             transposing LDS reads turn into k-contiguous MFMA
+//                             operands; the epilogue only stores X' into the other
+//                             ping-pong buffer, or the final U to the caller.
 // Folding a into B' removes every epilogue read from the largest product; it
 // rounds a + B_ii to the compute dtype once instead of rounding B_ii.
 // All workspace dims are multiples of 256, zero-padded, so the main loop needs no
@@ -24,7 +25,7 @@
 // bf16 or 32 fp32 of k) of both operands, each one contiguous k-block of the
 // workspace layout, straight from HBM/L2 into LDS with 16-byte buffer loads that
 // write LDS directly (no register staging), through a 2-stage ring: the loads of
-// slab t+1 are in flight while slab t is multiplied.  LDS rows are 128 bytes with
+// slab t+2 are issued early in slab t+1 and land while it is multiplied.  LDS rows are 128 bytes with
 // the 16-byte chunk index XOR-swizzled by (r ^ r>>1) & 7, so the fragment reads of
 // 8 or 16 consecutive rows hit distinct banks.
 #pragma once
