@@ -455,7 +455,7 @@ int32_t sign_pack(const void* u, int32_t dtype, int64_t numel, uint32_t* packed,
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!u || !packed) return fail(MO_ERR_INVALID, "u or packed is NULL");
   const int64_t threads = ((numel + 31) / 32) * 4;
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (threads + 256 * PACK_UNITS - 1) / (256 * PACK_UNITS);
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int vec = aligned16(u) ? 1 : 0;
@@ -507,7 +507,7 @@ int32_t sign_unpack(const uint32_t* packed, int64_t numel, int32_t dtype, void* 
   if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !out) return fail(MO_ERR_INVALID, "packed or out is NULL");
-  const int64_t blocks = ((numel + 7) / 8 + 255) / 256;
+  const int64_t blocks = ((numel + 7) / 8 + 256 * UNPACK_UNITS - 1) / (256 * UNPACK_UNITS);
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int vec = aligned16(out) ? 1 : 0;
@@ -528,7 +528,7 @@ int32_t sign_apply(const uint32_t* packed, int64_t numel, int32_t dtype, void* w
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !weight) return fail(MO_ERR_INVALID, "packed or weight is NULL");
   if (!std::isfinite(lr)) return fail(MO_ERR_INVALID, "lr must be finite");
-  const int64_t blocks = ((numel + 7) / 8 + 255) / 256;
+  const int64_t blocks = ((numel + 7) / 8 + 256 * SAPPLY_UNITS - 1) / (256 * SAPPLY_UNITS);
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int vec = aligned16(weight) ? 1 : 0;
