@@ -19,13 +19,13 @@
 //
 // Tiling (gfx950, wave64): 256x256 block tile; NWAVES = 8 waves in a 2 x 4 grid,
 // each owning a 128 x 64 sub-tile = 4 x 2 MFMA 32x32 blocks (128 fp32 accumulators
-// per lane), two waves per SIMD so that twice as many operand loads are in flight
-// as with 4 waves of 128 x 128 (the operand stream into LDS, not the MFMA rate, is
-// what bounds this kernel).  The k-loop streams slabs of 256 rows x 128 bytes (64
-// bf16 or 32 fp32 of k) of both operands, each one contiguous k-block of the
-// workspace layout, straight from HBM/L2 into LDS with 16-byte buffer loads that
-// write LDS directly (no register staging), through a 2-stage ring: the loads of
-// slab t+2 are issued early in slab t+1 and land while it is multiplied.  LDS rows are 128 bytes with
+// per lane), two waves per SIMD: with bf16 operands one of them issues the slab
+// loads for both while the other keeps the SIMD's matrix core busy (see the loader
+// waves below).  The k-loop streams slabs of 256 rows x 128 bytes (64 bf16 or 32
+// fp32 of k) of both operands, each one contiguous k-block of the workspace layout,
+// straight from HBM/L2 into LDS with 16-byte buffer loads that write LDS directly
+// (no register staging), through a 2-stage ring: the loads of slab t+2 are issued
+// early in slab t+1 and land while it is multiplied.  LDS rows are 128 bytes with
 // the 16-byte chunk index XOR-swizzled by (r ^ r>>1) & 7, so the fragment reads of
 // 8 or 16 consecutive rows hit distinct banks.
 #pragma once
