@@ -192,17 +192,27 @@ __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict
   const int64_t item = static_cast<int64_t>(blockIdx.x) * MP_TPB;
   const MatDesc& d = descs[find_desc(descs, count, KIND_PREP, item)];
   const int64_t local = item - d.begin[KIND_PREP];
-  const int tn = d.np / PREP_TILE;
-  const int i0 = static_cast<int>(local / tn) * PREP_TILE;    // rows of X
-  const int jb = static_cast<int>(local % tn) * PREP_TILE;    // first column of X; tile u at jb + 64u
+  // A block's tiles run along the source's rows, so each source row is read in
+  // MP_TPB * 256-byte runs: tiles u at X columns jb + 64u when X = S (rows of X are
+  // rows of S), at X rows ib + 64u when X = S^T (rows of X are columns of S), with
+  // consecutive blocks moving along that same direction.  For S^T this also writes
+  // 256 consecutive rows of one k-block of X.  Measured at the 7B-class set (its 32
+  // transposed matrices hold 22% of the elements): 14.7-15.8 -> 13.4-13.7 ms per
+  // pass against tiles along X columns for both orientations.
+  const bool along_rows = d.transposed;
+  const int tn = d.np / PREP_TILE, tmr = d.mp / PREP_TILE;
+  const int ib = along_rows ? static_cast<int>(local % tmr) * PREP_TILE : static_cast<int>(local / tn) * PREP_TILE;
+  const int jb = along_rows ? static_cast<int>(local / tmr) * PREP_TILE : static_cast<int>(local % tn) * PREP_TILE;
+  auto tile_i0 = [&](int u) { return along_rows ? ib + PREP_TILE * u : ib; };   // rows of X
+  auto tile_j0 = [&](int u) { return along_rows ? jb : jb + PREP_TILE * u; };   // columns of X
   const int t = threadIdx.x;
   const int64_t ld = d.cols;
   const int64_t rlim = d.rows, clim = d.cols;
   const TG* __restrict__ g = static_cast<const TG*>(d.grad);
   float* __restrict__ m = d.mom;
   // source rows/cols of tile u: X[i][j] = S[i][j] (not transposed) or S[j][i]
-  auto src_r0 = [&](int u) { return d.transposed ? jb + PREP_TILE * u : i0; };
-  auto src_c0 = [&](int u) { return d.transposed ? i0 : jb + PREP_TILE * u; };
+  auto src_r0 = [&](int u) { return d.transposed ? tile_j0(u) : tile_i0(u); };
+  auto src_c0 = [&](int u) { return d.transposed ? tile_i0(u) : tile_j0(u); };
   bool inside = d.vec_ok;
 #pragma unroll
   for (int u = 0; u < MP_TPB; ++u)
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < MP_TPB; ++u) write_operand_tile<TC>(d, i0, jb + PREP_TILE * u, tile[u]);
+  for (int u = 0; u < MP_TPB; ++u) write_operand_tile<TC>(d, tile_i0(u), tile_j0(u), tile[u]);
   ss = block_sum_256(ss);
   if (t < MP_TPB) partial[item + t] = t == 0 ? ss : 0.0;
 }
