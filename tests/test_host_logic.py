@@ -96,6 +96,42 @@ def test_profsummary_round_trip(tmp_path):
     assert h == profsummary.code_hash()
 
 
+def test_profsummary_kind_names():
+    """Every kernel the library launches maps to the kind name the benchmark's per-kernel
+    table, roofline and traffic lookup use (mangled names as hipcc emits them)."""
+    names = {
+        "_ZN2mo9k_ns_gemmIDF16bLi0EDF16bEEvPKNS_7MatDescEilifffPKf": "ns_syrk",
+        "_ZN2mo9k_ns_gemmIDF16bLi1EDF16bEEvPKNS_7MatDescEilifffPKf": "ns_poly",
+        "_ZN2mo9k_ns_gemmIDF16bLi2EDF16bEEvPKNS_7MatDescEilifffPKf": "ns_apply",
+        "_ZN2mo9k_ns_gemmIfLi3EfEEvPKNS_7MatDescEilifffPKf": "ns_apply",
+        "_ZN2mo9k_ns_gemmIDF16bLi4EDF16bEEvPKNS_7MatDescEilifffPKf": "ns_apply",
+        "_ZN2mo15k_momentum_prepIDF16bDF16bLb1EEEvPKNS_7MatDescEifPd": "momentum_prep",
+        "_ZN2mo16k_momentum_sumsqIDF16bLb1EEEvPKNS_7MatDescEifPd": "momentum_sumsq",
+        "_ZN2mo11k_prep_redoIfDF16bEEvPKNS_7MatDescEiPKfPKii": "prep_operand",
+        "_ZN2mo12k_norm_scaleEPKNS_7MatDescEPKdifPfS5_Pi": "norm_scale",
+        "_ZN2mo13k_scaled_copyIfDF16bEEvPKNS_7MatDescEiPKfiif": "scaled_copy",
+        "_ZN2mo11k_sign_packIfEEvPKT_lPji": "sign_pack",
+        "_ZN2mo11k_sign_voteILi4ELb0EEEvPKjillPjPai": "sign_vote",
+        "_ZN2mo13k_sign_unpackIDF16bEEvPKjlPT_i": "sign_unpack",
+        "_ZN2mo12k_sign_applyIfEEvPKjlPT_fi": "sign_apply",
+    }
+    for mangled, kind in names.items():
+        assert profsummary.kind_of(mangled) == kind, mangled
+    # the library's own profiling records use the same kind names
+    for kind in set(names.values()):
+        assert kind in bench_kinds()
+
+
+def bench_kinds():
+    """Kind names the library's per-kernel timing reports (mo_profile_end)."""
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..", "matrix_optimizers_sharded_amd", "csrc",
+                            "matopt.hip")).read()
+    block = src[src.index("kKindNames[] = {"):]
+    block = block[:block.index("};")]
+    return set(re.findall(r'"([a-z_]+)"', block))
+
+
 def test_profsummary_mfma(tmp_path):
     path = tmp_path / "m.csv"
     hdr = "Dispatch_Id,Grid_Size,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
