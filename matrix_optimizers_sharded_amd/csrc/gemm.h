@@ -654,7 +654,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       // LDS staging slab instead: a round puts 32 columns j x 128 bytes of
       // rows i there in [j][i] order (16-byte chunks XOR-swizzled by j & 7) and sends
       // them out as whole 128-byte lines, 8 rows per instruction.  POLY needs b*A at
-      // [ib..ib+3][j], read as one vector from A[j][ib..] (A is symmetric).
+      // [ib..ib+3][j].
       typedef typename Vec4<T>::type v4_t;
       if (MODE != GM_APPLY_FINAL && MODE != GM_APPLY_WEIGHT) {
         constexpr int AP = 128 / (32 * static_cast<int>(sizeof(T)));   // MFMA row blocks per 128 bytes of k
@@ -687,8 +687,16 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             }
           }
         };
-        // A[j][ib..ib+3]: four consecutive k of one row, inside one k-block
-        auto load_e = [&](int ib, int j) { return *at<const v4_t>(Ain, kb_off<T>(j, ib, d.pM)); };
+        // A[ib..ib+3][j] for bA, read by rows: A is stored exactly symmetric, and with
+        // consecutive lanes on consecutive j each element load covers 64 contiguous
+        // bytes of each of 2 rows.  (The one vector load of A[j][ib..ib+3] per lane it
+        // replaces touched 32 rows per instruction; POLY -0.8%.)
+        auto load_e = [&](int ib, int j) {
+          v4_t e;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) e[t] = *at<const T>(Ain, kb_off<T>(ib + t, j, d.pM));
+          return e;
+        };
         unsigned char* stg = staging + wave * 4096;
 #pragma unroll
         for (int p = 0; p < 4 / AP; ++p)
