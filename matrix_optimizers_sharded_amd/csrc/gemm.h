@@ -68,13 +68,13 @@ constexpr int NSTAGE = 2;
 constexpr int OPERAND_BYTES = GT * ROW_BYTES;
 constexpr int STAGE_BYTES = 2 * OPERAND_BYTES;         // P and Q
 constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
-#ifndef MO_GEMM_WAVES
-#define MO_GEMM_WAVES 8
-#endif
-constexpr int NWAVES = MO_GEMM_WAVES;                  // 8 (4 builds and is slower)
+// 8 waves, two per SIMD.  APPLY's transposed slab layout needs a multiple of the 8
+// row groups of a bf16 k-block (a 4-wave grid of 128 x 128 sub-tiles measured 2.7%
+// slower before that layout existed).
+constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WAVES_N = NWAVES / 2;                    // wave grid: 2 x WAVES_N
-constexpr int WAVE_N = GT / WAVES_N;                   // columns per wave: 128 or 64
+constexpr int WAVE_N = GT / WAVES_N;                   // columns per wave: 64
 constexpr int NB = WAVE_N / 32;                        // 32-column MFMA blocks per wave
 constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;        // rows one 1 KiB wave load fills
 constexpr int INST_PER_OPERAND = OPERAND_BYTES / 1024 / NWAVES;  // per wave, per slab
@@ -359,7 +359,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   constexpr int KR = KB;                                         // k rows per slab
   constexpr int JB = GT / KB;                                    // k-blocks per tile width
   constexpr int RG = KR / 8;                                     // 8-row groups per k-block
-  static_assert(ROW_BYTES == 128 && NWAVES % RG == 0, "transposed slab layout assumes 128-byte k-blocks");
+  static_assert(ROW_BYTES == 128 && NWAVES % RG == 0,
+                "transposed slab layout: 128-byte k-blocks, waves a multiple of the row groups");
   const int qrow = (wave % RG) * 8 + lane / 8;   // k row of this lane's loads within the slab
   const uint32_t qlane = static_cast<uint32_t>(qrow) * ROW_BYTES + (((lane % 8) ^ swz_tr(qrow)) << 4);
 
