@@ -167,24 +167,21 @@ __device__ inline void write_operand_tile(const MatDesc& d, int i0, int j0,
   }
 }
 
-// The fused first pass of a step with at least one NS iteration, MP_TPB consecutive
-// 64x64 tiles of one row of the padded oriented operand per block (256 threads;
-// items per matrix are a multiple of 16 and tiles per operand row of 4, so a
-// block's tiles never cross a row or a matrix): with MOMENTUM, M <- fma(beta, M, G)
-// in place over the tiles' source elements; X = M (or the input), unscaled, in the
-// compute dtype, zero outside the m x n corner; and the block's fp64 sum of squares
-// to partial[first item] (0 to the others).  One HBM sweep: G and M read once, M
-// and X written once.  The Frobenius scale s comes afterwards, applied by the first
-// NS products (s^2 on X X^T, s on the first B X), which in exact arithmetic is the
-// same as scaling X first: (sX)(sX)^T = s^2 X X^T and B'(sX) = s B'X.
+// The fused first pass of a step with at least one NS iteration, MP_TPB = 4 64x64
+// tiles of the padded oriented operand per block (256 threads; the item count of
+// every matrix is a multiple of 16 and its tile grid a multiple of 4 in each
+// direction, so a block's tiles never leave their matrix): with MOMENTUM,
+// M <- fma(beta, M, G) in place over the tiles' source elements; X = M (or the
+// input), unscaled, in the compute dtype, zero outside the m x n corner; and the
+// block's fp64 sum of squares to partial[first item] (0 to the others).  One HBM
+// sweep: G and M read once, M and X written once.  The Frobenius scale s comes
+// afterwards, applied by the first NS products (s^2 on X X^T, s on the first B X),
+// which in exact arithmetic is the same as scaling X first: (sX)(sX)^T = s^2 X X^T
+// and B'(sX) = s B'X.
 // Four tiles per block (2 blocks per CU by LDS) measured fastest: 5.1-5.7 TB/s
 // against 4.7-5.3 TB/s with one tile per block at the 7B-class owner set, as more
 // of each thread's loads are in flight before its first store.
-#ifndef MO_MP_TPB
-#define MO_MP_TPB 4
-#endif
-constexpr int MP_TPB = MO_MP_TPB;
-static_assert(MP_TPB == 1 || MP_TPB == 2 || MP_TPB == 4, "tiles per block: 1, 2 or 4");
+constexpr int MP_TPB = 4;
 template <typename TG, typename TC, bool MOMENTUM>
 __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict__ descs, int count,
                                                        float beta, double* __restrict__ partial) {
@@ -192,19 +189,24 @@ __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict
   const int64_t item = static_cast<int64_t>(blockIdx.x) * MP_TPB;
   const MatDesc& d = descs[find_desc(descs, count, KIND_PREP, item)];
   const int64_t local = item - d.begin[KIND_PREP];
-  // A block's tiles run along the source's rows, so each source row is read in
-  // MP_TPB * 256-byte runs: tiles u at X columns jb + 64u when X = S (rows of X are
-  // rows of S), at X rows ib + 64u when X = S^T (rows of X are columns of S), with
-  // consecutive blocks moving along that same direction.  For S^T this also writes
-  // 256 consecutive rows of one k-block of X.  Measured at the 7B-class set (its 32
-  // transposed matrices hold 22% of the elements): 14.7-15.8 -> 13.4-13.7 ms per
-  // pass against tiles along X columns for both orientations.
+  // Tile arrangement (MP_TPB = 4 tiles per block, consecutive blocks next to each
+  // other along the source's rows):
+  //   X = S^T (rows of X are columns of S): tiles u at X rows ib + 64u, so each row
+  //     of S is read in 1 KiB runs and 256 consecutive rows of one k-block of X are
+  //     written; against tiles along X columns 14.7-15.8 -> 13.4-13.7 ms per pass at
+  //     the 7B-class set (its transposed matrices hold 22% of the elements).
+  //   X = S: a 2 x 2 group (128 x 128 of X): 512-byte runs of S's rows, and 128
+  //     consecutive rows in each of two k-blocks of X; against 1 x 4 tiles along X
+  //     columns (1 KiB runs, four k-blocks) 14.5-15.4 -> 13.3-13.6 ms, one box.
   const bool along_rows = d.transposed;
-  const int tn = d.np / PREP_TILE, tmr = d.mp / PREP_TILE;
-  const int ib = along_rows ? static_cast<int>(local % tmr) * PREP_TILE : static_cast<int>(local / tn) * PREP_TILE;
-  const int jb = along_rows ? static_cast<int>(local / tmr) * PREP_TILE : static_cast<int>(local % tn) * PREP_TILE;
-  auto tile_i0 = [&](int u) { return along_rows ? ib + PREP_TILE * u : ib; };   // rows of X
-  auto tile_j0 = [&](int u) { return along_rows ? jb : jb + PREP_TILE * u; };   // columns of X
+  const int tn = d.np / PREP_TILE, tmr = d.mp / PREP_TILE;   // multiples of 4
+  const int64_t grp = local / 4;                               // 2 x 2 groups over (tmr/2) x (tn/2)
+  const int ib = along_rows ? static_cast<int>(local % tmr) * PREP_TILE
+                            : static_cast<int>(grp / (tn / 2)) * 2 * PREP_TILE;
+  const int jb = along_rows ? static_cast<int>(local / tmr) * PREP_TILE
+                            : static_cast<int>(grp % (tn / 2)) * 2 * PREP_TILE;
+  auto tile_i0 = [&](int u) { return along_rows ? ib + PREP_TILE * u : ib + PREP_TILE * (u >> 1); };  // rows of X
+  auto tile_j0 = [&](int u) { return along_rows ? jb : jb + PREP_TILE * (u & 1); };                 // cols of X
   const int t = threadIdx.x;
   const int64_t ld = d.cols;
   const int64_t rlim = d.rows, clim = d.cols;
