@@ -104,6 +104,82 @@ def traffic_of(kind, workload):
     return val
 
 
+def smi_sample():
+    """GPU socket power (W) and the mean graphics clock over the XCDs (MHz), read
+    once by `amd-smi metric -p -c` in a child process while queued GPU work runs.
+    None where the tool is missing or prints something else."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                             timeout=20).stdout
+    except Exception:
+        return None
+    power = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    clks = [float(v) for v in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", txt)]
+    if not power and not clks:
+        return None
+    return {"socket_power_w": float(power.group(1)) if power else None,
+            "gfx_clock_mhz": round(sum(clks) / len(clks), 1) if clks else None}
+
+
+def blas_ceiling(torch, dev, seconds=2.0):
+    """What the vendor GEMM library (torch.matmul -> hipBLASLt) sustains on the NS
+    product shapes on this same GPU, as a measured ceiling for the hand-written
+    kernels.  Dense products, so the flop count is the full 2*m*n*k (no symmetry
+    saving).  A calibration only: the library's step never calls it."""
+    # (dtype, m, n, k, layout, what): "nn" multiplies row-major (m x k) by row-major
+    # (k x n); "nt" multiplies row-major (m x k) by the transpose of a row-major
+    # (n x k), the layout of X X^T
+    cases = [("bf16", 4096, 11008, 4096, "nn", "B X at 4096 x 11008 (APPLY-like, K = 4096)"),
+             ("bf16", 4096, 11008, 4096, "nt", "the same product with the second operand k-contiguous"),
+             ("bf16", 4096, 4096, 11008, "nt", "X X^T at 4096 x 11008 (SYRK-like, K = 11008, dense)"),
+             ("bf16", 4096, 4096, 4096, "nt", "A A^T at 4096^2 (POLY-like, dense)"),
+             ("bf16", 768, 3072, 768, "nn", "B X at 768 x 3072 (K = 768)"),
+             ("f32", 4096, 4096, 4096, "nt", "A A^T at 4096^2, fp32")]
+    torch.backends.cuda.matmul.allow_tf32 = False
+    out = []
+    for dt, m, n, k, layout, what in cases:
+        dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        a = torch.randn(m, k, generator=gen, device=dev).to(dtype)
+        if layout == "nn":
+            b = torch.randn(k, n, generator=gen, device=dev).to(dtype)
+        else:
+            b = torch.randn(n, k, generator=gen, device=dev).to(dtype).t()
+        c = torch.empty(m, n, device=dev, dtype=dtype)
+        # about a second of back-to-back products first, so the clock has settled
+        # where a long GEMM-bound step runs, then about two seconds timed
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        est = max(time.perf_counter() - t0, 1e-5)
+        for _ in range(int(1.0 / est) + 1):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        reps = max(int(seconds / est), 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        time.sleep(seconds / 2)
+        smi = smi_sample()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * m * n * k / (ms / 1e3) / 1e12
+        peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS
+        out.append({"dtype": dt, "m": m, "n": n, "k": k, "layout": layout, "what": what, "ms": round(ms, 4),
+                    "reps": reps, "tflops": round(tf, 1), "frac": round(tf / peak, 4), "smi": smi})
+        print(f"[bench] torch.matmul {what}: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}%), {smi}",
+              file=sys.stderr, flush=True)
+        del a, b, c
+    return out
+
+
 def cpu_baseline(wid, iters):
     """The fp64 oracle on a bounded sample of the workload, on the host cores."""
     import numpy as np
@@ -154,6 +230,10 @@ def main():
     ap.add_argument("--apply", action="store_true",
                     help="time muon_step_apply (W <- W - lr*U fused into the last product, bf16 weights) "
                          "instead of muon_step_batched")
+    ap.add_argument("--smi", action="store_true",
+                    help="read GPU power and clock once (amd-smi) during the timed steps")
+    ap.add_argument("--blas-ceiling", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the NS product shapes: a measured ceiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -232,6 +312,11 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
+    smi = None
+    if args.smi:
+        # every step is queued: sample power and clock while they run
+        time.sleep(1.0)
+        smi = smi_sample()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kernels = mo.profile_end()
@@ -286,6 +371,8 @@ def main():
     if tail_numel:
         sign_tail = measure_sign_tail(mo, torch, dev, tail_numel)
 
+    ceiling = blas_ceiling(torch, dev) if args.blas_ceiling else None
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -316,6 +403,10 @@ def main():
         "cpu_baseline": cpu,
         "sign_tail": sign_tail,
     }
+    if ceiling is not None:
+        line["blas_ceiling"] = ceiling
+    if smi is not None:
+        line["smi_during_steps"] = smi
     print(json.dumps(line), flush=True)
 
 
