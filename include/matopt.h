@@ -112,6 +112,26 @@ int32_t muon_step_batched(const mo_matrix *mats, int32_t count, int32_t grad_dty
                           const mo_ns_params *ns, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* Scratch held by each GPU for muon_step_batched_noalloc: 256 MiB, enough for one
+ * 4096 x 11008 matrix in bf16 (about 236 MiB) or for sets of smaller ones. */
+#define MO_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same step as muon_step_batched,
+ * with the same arguments and bit-identical results, but without a caller
+ * workspace.  Its scratch is a file-scope device array of MO_NOALLOC_SCRATCH_BYTES
+ * that every GPU the library runs on holds until the process ends; the call
+ * allocates nothing (no hipMalloc, no pinned staging: the descriptor table goes up
+ * through kernel arguments) and records no profiling events.  A list whose
+ * muon_workspace_bytes exceeds MO_NOALLOC_SCRATCH_BYTES is rejected with
+ * MO_ERR_WORKSPACE before anything is launched.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (two streams, two threads) race and
+ * must be ordered by the caller; the scratch keeps the last call's contents, and
+ * nothing in it needs to start at zero. */
+int32_t muon_step_batched_noalloc(const mo_matrix *mats, int32_t count, int32_t grad_dtype,
+                                  int32_t compute_dtype, int32_t out_dtype, float beta,
+                                  const mo_ns_params *ns, void *stream);
+
 /* Frobenius scaling and Newton-Schulz only (no momentum): out <- NS(x / (||x|| + eps)).
  * in_dtype: MO_F32 or MO_BF16.  x == out is allowed. */
 int32_t ns_orthogonalize(const mo_matrix *mats, int32_t count, int32_t in_dtype,

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     load_library,
     library_path,
     muon_step_batched,
+    muon_step_batched_noalloc,
     muon_step_apply,
     ns_orthogonalize,
     sign_pack,
@@ -26,4 +27,5 @@ from .binding import (  # noqa: F401
     Workspace,
     MO_F32,
     MO_BF16,
+    NOALLOC_SCRATCH_BYTES,
 )

@@ -11,6 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 MO_F32, MO_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 256 << 20   # MO_NOALLOC_SCRATCH_BYTES in include/matopt.h
 ERRORS = {-1: "MO_ERR_INVALID", -2: "MO_ERR_UNSUPPORTED", -3: "MO_ERR_WORKSPACE", -4: "MO_ERR_HIP"}
 
 
@@ -63,6 +64,9 @@ def load_library():
     lib.sign_pack.restype = I32
     lib.sign_vote.argtypes = [P, I32, I64, P, P, P]
     lib.sign_vote.restype = I32
+    lib.muon_step_batched_noalloc.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32, F,
+                                              ctypes.POINTER(MoNsParams), P]
+    lib.muon_step_batched_noalloc.restype = I32
     lib.muon_step_apply.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32, F,
                                     ctypes.POINTER(MoNsParams), F, P, SZ, P]
     lib.muon_step_apply.restype = I32
@@ -213,6 +217,34 @@ def muon_step_batched(grads, moms, outs, beta, a, b, c, iters, eps=1e-7, compute
         _check(lib.muon_step_batched(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute),
                                      _dtype_code(odt), float(beta), ctypes.byref(ns), ws.data_ptr(),
                                      ws.numel(), _stream_ptr(grads[0])))
+
+
+def muon_step_batched_noalloc(grads, moms, outs, beta, a, b, c, iters, eps=1e-7, compute=None):
+    """muon_step_batched without a workspace: the library's own fixed device scratch
+    (MO_NOALLOC_SCRATCH_BYTES per GPU) is used and nothing is allocated, here or in
+    the library.  Lists needing more scratch raise MatoptError (MO_ERR_WORKSPACE)."""
+    import torch
+    lib = load_library()
+    if compute is None:
+        compute = torch.bfloat16
+    shapes = [tuple(g.shape) for g in grads]
+    if not (len(grads) == len(moms) == len(outs)):
+        raise MatoptError(-1, "grads, moms and outs must have the same length")
+    if not shapes:
+        return
+    _validate(grads, shapes, "grads", (torch.float32, torch.bfloat16))
+    _validate(moms, shapes, "moms", (torch.float32,))
+    _validate(outs, shapes, "outs", (torch.float32, torch.bfloat16))
+    gdt, odt = grads[0].dtype, outs[0].dtype
+    if any(g.dtype != gdt for g in grads) or any(o.dtype != odt for o in outs):
+        raise MatoptError(-2, "all grads (and all outs) must share one dtype")
+    dev = _one_device(grads, moms, outs)
+    mats = _mats(shapes, grads=grads, moms=moms, outs=outs)
+    ns = _ns_params(a, b, c, iters, eps)
+    with _on(dev):
+        _check(lib.muon_step_batched_noalloc(mats, len(shapes), _dtype_code(gdt), _dtype_code(compute),
+                                             _dtype_code(odt), float(beta), ctypes.byref(ns),
+                                             _stream_ptr(grads[0])))
 
 
 def muon_step_apply(grads, moms, weights, beta, a, b, c, iters, lr, eps=1e-7, compute=None,

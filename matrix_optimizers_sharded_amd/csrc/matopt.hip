@@ -37,7 +37,31 @@
 
 using namespace mo;
 
+// Scratch of the allocation-free entry point (muon_step_batched_noalloc): the
+// descriptor table, scalars, partial sums and X/A/B operands live here instead of
+// in a caller workspace.  Each GPU the library is loaded on holds its own copy for
+// the life of the process.  Host code never uses this name as an address: the
+// per-device address comes from hipGetSymbolAddress (scratch_base below).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MO_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Descriptor upload through kernel arguments, DESC_ARG descriptors per launch: the
+// runtime copies the argument block into its own kernel-argument memory, so this
+// needs no pinned staging buffer, no host wait and no allocation.
+constexpr int DESC_ARG = 16;
+struct DescArg {
+  MatDesc d[DESC_ARG];
+};
+static_assert(sizeof(DescArg) <= 4000, "kernel argument block too large");
+static_assert(sizeof(MatDesc) % 4 == 0, "descriptors are copied as 32-bit words");
+
+__global__ __launch_bounds__(256) void k_store_descs(DescArg a, int n, MatDesc* __restrict__ dst) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(&a.d[0]);
+  uint32_t* out = reinterpret_cast<uint32_t*>(dst);
+  const int words = n * static_cast<int>(sizeof(MatDesc) / 4);
+  for (int i = threadIdx.x; i < words; i += blockDim.x) out[i] = src[i];
+}
 
 thread_local std::string g_err;
 
@@ -227,10 +251,14 @@ hipEvent_t take_event() {
 }
 
 // Launch helper: optional event bracket + launch error check.
+// Set for the duration of an allocation-free call: its launches record no profiling
+// events (creating one may allocate).
+thread_local bool g_no_events = false;
+
 template <typename F>
 int launch(int pk, hipStream_t stream, F&& f) {
   ProfRec rec{pk, nullptr, nullptr};
-  const bool prof = g_prof.load();
+  const bool prof = g_prof.load() && !g_no_events;
   if (prof) {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     rec.e0 = take_event();
@@ -378,9 +406,55 @@ int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const S
   return run_step<TG, float, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
 }
 
+// Address of this device's copy of `scratch`, looked up once per device with that
+// device current and kept.
+std::atomic<void*> g_scratch_base[64];
+
+int scratch_base(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MO_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(MO_ERR_UNSUPPORTED, "device index above 63");
+  void* p = g_scratch_base[dev].load();
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MO_ERR_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch_base[dev].store(p);
+  }
+  *out = p;
+  return MO_OK;
+}
+
+int upload_by_args(MatDesc* dst, const MatDesc* src, int count, hipStream_t stream) {
+  for (int k0 = 0; k0 < count; k0 += DESC_ARG) {
+    const int n = std::min(DESC_ARG, count - k0);
+    DescArg a;
+    std::memset(&a, 0, sizeof(a));
+    std::memcpy(a.d, src + k0, sizeof(MatDesc) * n);
+    hipLaunchKernelGGL(k_store_descs, dim3(1), dim3(256), 0, stream, a, n, dst + k0);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(MO_ERR_HIP, std::string("descriptor upload failed: ") + hipGetErrorString(err));
+  }
+  return MO_OK;
+}
+
+// Switches event recording off for this thread while it lives (when `on`).
+struct NoEvents {
+  bool on;
+  explicit NoEvents(bool o) : on(o) {
+    if (on) g_no_events = true;
+  }
+  ~NoEvents() {
+    if (on) g_no_events = false;
+  }
+};
+
+// noalloc: the workspace is this device's `scratch` (workspace and ws_bytes are
+// ignored), the descriptor table goes up through kernel arguments, and no call
+// below allocates.
 int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out, bool momentum, float beta,
             const mo_ns_params* ns, void* workspace, size_t ws_bytes, void* stream_ptr,
-            const ApplyOpt& ap = ApplyOpt()) {
+            const ApplyOpt& ap = ApplyOpt(), bool noalloc = false) {
   g_err.clear();
   if (ap.on && !std::isfinite(ap.lr)) return fail(MO_ERR_INVALID, "lr must be finite");
   if (!ns) return fail(MO_ERR_INVALID, "ns params is NULL");
@@ -393,6 +467,13 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   Plan plan;
   MO_TRY(build_plan(mats, count, compute, momentum, nullptr, plan, in_dtype, out));
   if (count == 0) return MO_OK;
+  if (noalloc) {
+    if (plan.bytes > MO_NOALLOC_SCRATCH_BYTES)
+      return fail(MO_ERR_WORKSPACE, "the allocation-free step needs " + std::to_string(plan.bytes) +
+                                        " bytes of scratch; it holds " + std::to_string(MO_NOALLOC_SCRATCH_BYTES));
+    MO_TRY(scratch_base(&workspace));
+    ws_bytes = MO_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace) return fail(MO_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(workspace) & (ALIGN - 1)))
     return fail(MO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -408,7 +489,12 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   sc.first = sc.scale + count;
   sc.redo = reinterpret_cast<int*>(sc.first + count);
   sc.partial = reinterpret_cast<double*>(base + full.off_partial);
-  MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
+  const NoEvents quiet(noalloc);
+  if (noalloc) {
+    MO_TRY(upload_by_args(dd, full.descs.data(), count, stream));
+  } else {
+    MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
+  }
   if (in_dtype == MO_BF16)
     return dispatch_compute_out<bf16_t>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
   return dispatch_compute_out<float>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
@@ -430,6 +516,12 @@ int32_t muon_step_batched(const mo_matrix* mats, int32_t count, int32_t grad_dty
                           size_t workspace_bytes, void* stream) {
   return batched(mats, count, grad_dtype, compute_dtype, out_dtype, true, beta, ns, workspace, workspace_bytes,
                  stream);
+}
+
+int32_t muon_step_batched_noalloc(const mo_matrix* mats, int32_t count, int32_t grad_dtype, int32_t compute_dtype,
+                                  int32_t out_dtype, float beta, const mo_ns_params* ns, void* stream) {
+  return batched(mats, count, grad_dtype, compute_dtype, out_dtype, true, beta, ns, nullptr, 0, stream, ApplyOpt(),
+                 true);
 }
 
 int32_t muon_step_apply(const mo_matrix* mats, int32_t count, int32_t grad_dtype, int32_t compute_dtype,

@@ -140,3 +140,19 @@ def test_next_row_calls_validate_arguments(lib):
     assert lib.sign_unpack(None, 10, 1, fake, None) == -1
     assert lib.sign_apply(fake, 10, 1, None, ctypes.c_float(0.1), None) == -1
     assert lib.sign_apply(fake, 10, 1, fake, ctypes.c_float(float("nan")), None) == -1
+
+
+def test_noalloc_rejects_lists_beyond_its_scratch_on_the_host(lib):
+    """The allocation-free step checks its scratch bound on the host, before any
+    HIP call: two 4096^2 matrices in bf16 need more than MO_NOALLOC_SCRATCH_BYTES."""
+    ns = MoNsParams(3.4445, -4.775, 2.0315, 5, 1e-7)
+    m = mats((4096, 4096), (4096, 4096))
+    for i in range(2):
+        m[i].grad, m[i].momentum, m[i].out = 0x1000, 0x2000, 0x3000
+    need = lib.muon_workspace_bytes(m, 2, binding.MO_BF16)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.muon_step_batched_noalloc(m, 2, 1, 1, 1, 0.9, ctypes.byref(ns), None) == -3
+    assert b"allocation-free" in lib.mo_last_error()
+    text = open(HEADER).read()
+    assert re.search(r"#define MO_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", text)
+    assert binding.NOALLOC_SCRATCH_BYTES == 256 << 20
