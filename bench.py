@@ -8,9 +8,12 @@ sign-vote workload's step is ns_orthogonalize over the 8 worker momenta followed
 sign_pack per worker and one sign_vote.
 
 Prints ONE JSON line: matrix params/s (value), achieved TFLOP/s and % of the dense
-bf16 MFMA peak, a per-kernel breakdown from HIP events recorded by the library on the
-launch stream, the roofline of the dominant kernel and the fp64 CPU oracle timed on
-a bounded sample.
+MFMA peak of the compute dtype, a per-kernel breakdown from HIP events recorded by
+the library on the launch stream, the roofline of the dominant kernel, the same
+figures for the other owner sets (other_workloads: 125M-class, 1B-class, the
+Sign-Muon vote set, the single 256x128 fp32 matrix, and the 1B-class set with fp32
+compute) and the fp64 CPU oracle timed on the host cores.  --blas-ceiling adds
+what torch.matmul (hipBLASLt) sustains on the same product shapes.
 """
 
 import argparse
@@ -104,25 +107,6 @@ def traffic_of(kind, workload):
     return val
 
 
-def smi_sample():
-    """GPU socket power (W) and the mean graphics clock over the XCDs (MHz), read
-    once by `amd-smi metric -p -c` in a child process while queued GPU work runs.
-    None where the tool is missing or prints something else."""
-    import re
-    import subprocess
-    try:
-        txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
-                             timeout=20).stdout
-    except Exception:
-        return None
-    power = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
-    clks = [float(v) for v in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", txt)]
-    if not power and not clks:
-        return None
-    return {"socket_power_w": float(power.group(1)) if power else None,
-            "gfx_clock_mhz": round(sum(clks) / len(clks), 1) if clks else None}
-
-
 def blas_ceiling(torch, dev, seconds=2.0):
     """What the vendor GEMM library (torch.matmul -> hipBLASLt) sustains on the NS
     product shapes on this same GPU, as a measured ceiling for the hand-written
@@ -166,54 +150,192 @@ def blas_ceiling(torch, dev, seconds=2.0):
         for _ in range(reps):
             torch.matmul(a, b, out=c)
         e1.record()
-        time.sleep(seconds / 2)
-        smi = smi_sample()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         tf = 2.0 * m * n * k / (ms / 1e3) / 1e12
         peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS
         out.append({"dtype": dt, "m": m, "n": n, "k": k, "layout": layout, "what": what, "ms": round(ms, 4),
-                    "reps": reps, "tflops": round(tf, 1), "frac": round(tf / peak, 4), "smi": smi})
-        print(f"[bench] torch.matmul {what}: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}%), {smi}",
+                    "reps": reps, "tflops": round(tf, 1), "frac": round(tf / peak, 4)})
+        print(f"[bench] torch.matmul {what}: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}%)",
               file=sys.stderr, flush=True)
         del a, b, c
     return out
 
 
-def cpu_baseline(wid, iters):
-    """The fp64 oracle on a bounded sample of the workload, on the host cores."""
-    import numpy as np
-    import oracle
-    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, host_matrix, MUON_ABC, BETA, EPS
+def cpu_info():
+    """CPU model, logical core count and the BLAS library numpy calls (name, version,
+    threads) on this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = {"name": p.get("internal_api"), "version": p.get("version"),
+                        "threads": p.get("num_threads")}
+                break
     except Exception:
-        cores = os.cpu_count()
+        pass
+    return {"cpu_model": model, "logical_cores": os.cpu_count(), "blas": blas}
+
+
+def cpu_baseline(wid, iters):
+    """The fp64 oracle (numpy + the host BLAS), on the host cores, as a baseline.
+
+    Every distinct NS shape of the workload is timed once on its first matrix (a
+    tall matrix counts with its transpose: the oracle works on the wide
+    orientation); the whole owner set's time is the sum of those times weighted by
+    how many matrices share each shape, so the figure is extrapolated unless every
+    matrix was timed (the single-matrix workload)."""
+    import oracle
+    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, host_matrix, MUON_ABC, BETA, EPS
     w = WORKLOADS[wid]
     shapes = w.shapes
-    # sample: the first matrix of each distinct shape, capped to ~10-30 s of CPU work
-    seen, sample = set(), []
+    groups = {}
     for i, s in enumerate(shapes):
-        key = (min(s), max(s))
-        if key not in seen:
-            seen.add(key)
-            sample.append(i)
-    sample = sample[:2] if wid in (3, 4) else sample[:3]
-    params = 0
-    t0 = time.perf_counter()
-    for i in sample:
-        d = host_matrix(wid, i)
+        groups.setdefault((min(s), max(s)), []).append(i)
+    total_s, timed, parts = 0.0, 0, []
+    for key, idx in groups.items():
+        d = host_matrix(wid, idx[0])
+        t0 = time.perf_counter()
         if wid == 5:
             oracle.ns_orthogonalize(d["mom"], *MUON_ABC, iters, EPS)
         else:
             oracle.muon_step(d["grad"], d["mom"], BETA, *MUON_ABC, iters, EPS)
-        params += d["mom"].size
-    dt = time.perf_counter() - t0
-    desc = ", ".join(f"{shapes[i][0]}x{shapes[i][1]}" for i in sample)
-    return {"value": params / dt, "unit": "matrix params/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, {'NS' if wid == 5 else 'momentum + NS'}({iters}) on "
-                      f"matrices {desc} of the same workload, {dt:.1f} s"}
+        dt = time.perf_counter() - t0
+        total_s += dt * len(idx)
+        timed += 1
+        parts.append(f"{shapes[idx[0]][0]}x{shapes[idx[0]][1]} {dt:.2f} s x {len(idx)}")
+    info = cpu_info()
+    threads = (info["blas"] or {}).get("threads") or info["logical_cores"]
+    return {"value": w.numel / total_s, "unit": "matrix params/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": timed < w.count, "owner_set_seconds": round(total_s, 2),
+            "sample": f"fp64 numpy oracle, {'NS' if wid == 5 else 'momentum + NS'}({iters}): one matrix of each "
+                      f"distinct shape timed ({'; '.join(parts)}), weighted by how many matrices of the "
+                      f"{w.name} set have that shape",
+            **info}
+
+
+class Run:
+    """One workload resident on the device, with the step the benchmark times."""
+
+    def __init__(self, mo, torch, dev, wid, compute, apply=False):
+        from matrix_optimizers_sharded_amd.workloads import WORKLOADS, device_matrix, MUON_ABC, BETA, EPS
+        w = WORKLOADS[wid]
+        self.w, self.wid, self.compute = w, wid, compute
+        shapes = w.shapes
+        ws = mo.Workspace(dev)
+        self.ws = ws
+        if wid == 5:
+            moms = [device_matrix(5, i, dev)[1] for i in range(w.count)]
+            outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+            nwords = (shapes[0][0] * shapes[0][1] + 31) // 32
+            packed = torch.empty((w.count, nwords), dtype=torch.int32, device=dev)
+            vote = torch.empty(nwords, dtype=torch.int32, device=dev)
+            self.tensors = [moms, outs, packed, vote]
+
+            def step():
+                mo.ns_orthogonalize(moms, outs, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
+                for i in range(w.count):
+                    mo.sign_pack(outs[i], packed[i])
+                mo.sign_vote(packed, outs[0].numel(), out_packed=vote)
+        else:
+            grads, moms = [], []
+            for i in range(w.count):
+                g, m = device_matrix(wid, i, dev)
+                grads.append(g)
+                moms.append(m)
+            out_dtype = torch.bfloat16 if compute == torch.bfloat16 else torch.float32
+            if apply:
+                # weights: small values, updated in place every step
+                outs = [(torch.randn(s, device=dev) * 0.02).to(out_dtype) for s in shapes]
+
+                def step():
+                    mo.muon_step_apply(grads, moms, outs, BETA, *MUON_ABC, w.iters, 1e-3, EPS, compute=compute,
+                                       workspace=ws)
+            else:
+                outs = [torch.empty(s, dtype=out_dtype, device=dev) for s in shapes]
+
+                def step():
+                    mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute,
+                                         workspace=ws)
+            self.tensors = [grads, moms, outs]
+        self.step = step
+        torch.cuda.synchronize()
+
+    def time(self, mo, torch, steps, warmup, log=True):
+        """warmup untimed steps, then `steps` steps back to back between two device
+        synchronisations; per-kernel times from the library's HIP events."""
+        for i in range(warmup):
+            self.step()
+            torch.cuda.synchronize()
+            if log:
+                print(f"[bench] {self.w.name}: warmup {i + 1}/{warmup} done", file=sys.stderr, flush=True)
+        mo.profile_begin()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kernels = mo.profile_end()
+        return (t1 - t0) * 1000.0 / steps, kernels
+
+    def release(self, torch):
+        self.tensors = None
+        self.ws.buf = None
+        self.step = None
+        torch.cuda.empty_cache()
+
+
+def summarize(w, compute_bf16, ms, kernels, steps):
+    """TFLOP/s, % of the dtype's MFMA peak and a per-kernel breakdown for one timed
+    workload; returns (summary dict, per-launch helper)."""
+    shapes = w.shapes
+    flops = ns_flops(shapes, w.iters)
+    f_alg = sum(flops.values())
+    tflops = f_alg / (ms / 1000.0) / 1e12
+    peak = PEAK_BF16_TFLOPS if compute_bf16 else PEAK_F32_TFLOPS
+    es = 2 if compute_bf16 else 4
+    gb = 2 if w.grad_dtype == "bf16" else 4
+    hbm = hbm_bytes(shapes, 4 if w.wid == 5 else gb, es, momentum=(w.wid != 5))
+    if w.wid == 5:
+        one = shapes[0][0] * shapes[0][1]
+        hbm["sign_pack"] = w.count * one * (es + 1 / 8)
+        hbm["sign_vote"] = one * (w.count + 1) / 8
+
+    def per_launch(name):
+        launches, total = kernels[name]
+        lps = launches / steps
+        work = flops.get(name, hbm.get(name, 0.0)) / lps
+        return lps, total / launches, work
+
+    breakdown = {}
+    for name in kernels:
+        lps, pl_ms, work = per_launch(name)
+        entry = {"launches_per_step": lps, "ms_per_launch": round(pl_ms, 4), "ms_per_step": round(pl_ms * lps, 4)}
+        if name in flops:
+            entry["tflops"] = round(work / (pl_ms / 1e3) / 1e12, 2)
+        elif name in hbm:
+            entry["gbs"] = round(work / (pl_ms / 1e3) / 1e9, 1)
+        breakdown[name] = entry
+    out = {"ms_per_step": round(ms, 4), "params_per_s": w.numel / (ms / 1000.0), "tflops": round(tflops, 2),
+           "peak_tflops": peak, "frac": round(tflops / peak, 4), "flops_per_step": f_alg, "kernels": breakdown}
+    return out, per_launch, flops, hbm, peak
+
+
+# The owner sets timed besides the headline one (name, compute, steps, warmup):
+# every configuration of the benchmark, and the fp32 path on a multi-tile set.
+OTHER = [("125m-class", "bf16", 20, 3), ("1b-class-swiglu", "bf16", 10, 2), ("sign-vote-8x4096", "bf16", 10, 2),
+         ("single-256x128", "f32", 50, 5), ("1b-class-swiglu", "f32", 3, 1)]
 
 
 def main():
@@ -224,16 +346,18 @@ def main():
     ap.add_argument("--workload", default="7b-class", choices=sorted(NAMES))
     ap.add_argument("--compute", default=None, choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the named workload (by default the other owner sets follow it)")
     ap.add_argument("--sign-tail-numel", type=int, default=None,
                     help="also time sign_pack (fp32 input) and an 8-worker sign_vote on this many elements "
                          "(default: 2^28 for the sign-vote workload, off otherwise)")
     ap.add_argument("--apply", action="store_true",
                     help="time muon_step_apply (W <- W - lr*U fused into the last product, bf16 weights) "
                          "instead of muon_step_batched")
-    ap.add_argument("--smi", action="store_true",
-                    help="read GPU power and clock once (amd-smi) during the timed steps")
     ap.add_argument("--blas-ceiling", action="store_true",
                     help="also time torch.matmul (hipBLASLt) on the NS product shapes: a measured ceiling")
+    ap.add_argument("--blas-only", action="store_true",
+                    help="only the torch.matmul ceiling (for profiling the vendor kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -245,15 +369,18 @@ def main():
 
     import torch
     import matrix_optimizers_sharded_amd as mo
-    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, device_matrix, MUON_ABC, BETA, EPS
+    from matrix_optimizers_sharded_amd.workloads import WORKLOADS, MUON_ABC, BETA
+
+    dev = torch.device("cuda:0")
+    if args.blas_only:
+        print(json.dumps({"blas_ceiling": blas_ceiling(torch, dev)}), flush=True)
+        return
 
     wid = NAMES[args.workload]
     w = WORKLOADS[wid]
-    dev = torch.device("cuda:0")
     mo.load_library()
     compute_name = args.compute or w.compute
     compute = torch.bfloat16 if compute_name == "bf16" else torch.float32
-    shapes = w.shapes
     print(f"[bench] workload {w.name}: {w.count} matrices, {w.numel / 1e9:.3f} G params, compute {compute_name}",
           file=sys.stderr, flush=True)
 
@@ -265,94 +392,13 @@ def main():
         del src, dst
         print("[bench] 1 GiB calibration copy done", file=sys.stderr, flush=True)
 
-    ws = mo.Workspace(dev)
-    if wid == 5:
-        moms = [device_matrix(5, i, dev)[1] for i in range(w.count)]
-        outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
-        nwords = (shapes[0][0] * shapes[0][1] + 31) // 32
-        packed = torch.empty((w.count, nwords), dtype=torch.int32, device=dev)
-        vote = torch.empty(nwords, dtype=torch.int32, device=dev)
-
-        def step():
-            mo.ns_orthogonalize(moms, outs, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
-            for i in range(w.count):
-                mo.sign_pack(outs[i], packed[i])
-            mo.sign_vote(packed, outs[0].numel(), out_packed=vote)
-    else:
-        grads, moms = [], []
-        for i in range(w.count):
-            g, m = device_matrix(wid, i, dev)
-            grads.append(g)
-            moms.append(m)
-        out_dtype = torch.bfloat16 if compute == torch.bfloat16 else torch.float32
-        if args.apply:
-            # weights: small values, updated in place every step
-            outs = [(torch.randn(s, device=dev) * 0.02).to(out_dtype) for s in shapes]
-
-            def step():
-                mo.muon_step_apply(grads, moms, outs, BETA, *MUON_ABC, w.iters, 1e-3, EPS, compute=compute,
-                                   workspace=ws)
-        else:
-            outs = [torch.empty(s, dtype=out_dtype, device=dev) for s in shapes]
-
-            def step():
-                mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, w.iters, EPS, compute=compute,
-                                     workspace=ws)
-    torch.cuda.synchronize()
+    run = Run(mo, torch, dev, wid, compute, apply=args.apply)
     print("[bench] inputs resident", file=sys.stderr, flush=True)
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        print(f"[bench] warmup {i + 1}/{args.warmup} done (workspace {ws.buf.numel() / 2**30:.1f} GiB)",
-              file=sys.stderr, flush=True)
-
-    mo.profile_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    smi = None
-    if args.smi:
-        # every step is queued: sample power and clock while they run
-        time.sleep(1.0)
-        smi = smi_sample()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernels = mo.profile_end()
-    ms = (t1 - t0) * 1000.0 / args.steps
+    ms, kernels = run.time(mo, torch, args.steps, args.warmup)
+    run.release(torch)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    numel = w.numel
-    flops = ns_flops(shapes, w.iters)
-    f_alg = sum(flops.values())
-    tflops = f_alg / (ms / 1000.0) / 1e12
-    peak = PEAK_BF16_TFLOPS if compute == torch.bfloat16 else PEAK_F32_TFLOPS
-    es = 2 if compute == torch.bfloat16 else 4
-    gb = 2 if w.grad_dtype == "bf16" else 4
-    hbm = hbm_bytes(shapes, 4 if wid == 5 else gb, es, momentum=(wid != 5))
-
-    if wid == 5:
-        one = shapes[0][0] * shapes[0][1]
-        hbm["sign_pack"] = w.count * one * (es + 1 / 8)
-        hbm["sign_vote"] = one * (w.count + 1) / 8
-
-    def per_launch(name):
-        launches, total = kernels[name]
-        lps = launches / args.steps
-        work = flops.get(name, hbm.get(name, 0.0)) / lps
-        return lps, total / launches, work
-
-    breakdown = {}
-    for name in kernels:
-        lps, pl_ms, work = per_launch(name)
-        entry = {"launches_per_step": lps, "ms_per_launch": round(pl_ms, 4),
-                 "ms_per_step": round(pl_ms * lps, 4)}
-        if name in flops:
-            entry["tflops"] = round(work / (pl_ms / 1e3) / 1e12, 2)
-        elif name in hbm:
-            entry["gbs"] = round(work / (pl_ms / 1e3) / 1e9, 1)
-        breakdown[name] = entry
+    summary, per_launch, flops, hbm, peak = summarize(w, compute == torch.bfloat16, ms, kernels, args.steps)
     dom = max(kernels.items(), key=lambda kv: kv[1][1])[0] if kernels else None
     roofline = None
     if dom in flops:
@@ -371,16 +417,34 @@ def main():
     if tail_numel:
         sign_tail = measure_sign_tail(mo, torch, dev, tail_numel)
 
+    others = None
+    if not args.no_other_workloads:
+        others = []
+        for name, cname, steps, warmup in OTHER:
+            if name == w.name and cname == compute_name:
+                continue
+            ow = WORKLOADS[NAMES[name]]
+            oc = torch.bfloat16 if cname == "bf16" else torch.float32
+            r = Run(mo, torch, dev, ow.wid, oc)
+            oms, ok = r.time(mo, torch, steps, warmup, log=False)
+            r.release(torch)
+            osum = summarize(ow, oc == torch.bfloat16, oms, ok, steps)[0]
+            osum["kernels"] = {k: {kk: v[kk] for kk in ("ms_per_launch", "ms_per_step", "tflops", "gbs") if kk in v}
+                               for k, v in osum["kernels"].items()}
+            print(f"[bench] {name} ({cname}): {oms:.3f} ms/step, {osum['tflops']} TFLOP/s ({100 * osum['frac']:.1f}% "
+                  f"of {osum['peak_tflops']})", file=sys.stderr, flush=True)
+            others.append({"workload": name, "dtype": cname, "steps": steps, "warmup": warmup, **osum})
+
     ceiling = blas_ceiling(torch, dev) if args.blas_ceiling else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the fp64 CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        print("[bench] timing the fp64 CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wid, w.iters)
 
     line = {
         "metric": "NS-orthogonalized params/sec + MFMA TFLOP/s (% peak), 7B layer shapes",
-        "value": numel / (ms / 1000.0),
+        "value": w.numel / (ms / 1000.0),
         "unit": "matrix params/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -391,22 +455,21 @@ def main():
         "vs_baseline": None,
         "dtype": compute_name,
         "data": "synthetic",
-        "config": {"workload": w.name, "matrices": w.count, "params": numel, "ns_iters": w.iters,
+        "config": {"workload": w.name, "matrices": w.count, "params": w.numel, "ns_iters": w.iters,
                    "grad_dtype": w.grad_dtype, "momentum_dtype": "f32", "accumulate": "f32",
                    "coefficients": list(MUON_ABC), "beta": BETA, "parallelism": "single GPU (owner-local)",
                    "step": "muon_step_apply (W -= lr*U fused)" if args.apply else "muon_step_batched"},
-        "tflops": round(tflops, 2),
-        "pct_peak": round(100.0 * tflops / peak, 2),
-        "flops_per_step": f_alg,
-        "kernels": breakdown,
+        "tflops": summary["tflops"],
+        "pct_peak": round(100.0 * summary["frac"], 2),
+        "flops_per_step": summary["flops_per_step"],
+        "kernels": summary["kernels"],
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sign_tail": sign_tail,
+        "other_workloads": others,
     }
     if ceiling is not None:
         line["blas_ceiling"] = ceiling
-    if smi is not None:
-        line["smi_during_steps"] = smi
     print(json.dumps(line), flush=True)
 
 

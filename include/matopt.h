@@ -27,12 +27,14 @@
  *
  * Conventions for every call:
  *   - All buffer pointers are DEVICE pointers on the current HIP device, owned by
- *     the caller.  The library allocates no device memory on these calls; scratch
- *     comes from the caller's `workspace` (size from muon_workspace_bytes).  The
- *     only library-owned memory is a small pinned host staging ring for the
- *     per-call descriptor table, created on first use.
+ *     the caller.  The library allocates no device memory and no pinned host
+ *     memory on these calls; scratch comes from the caller's `workspace` (size
+ *     from muon_workspace_bytes), whose head receives the per-call descriptor
+ *     table through the kernel arguments of small copy kernels.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and the
  *     call returns without waiting for the GPU.  `mats` is read before return.
+ *     With profiling on (mo_profile_begin), calls also create and record HIP
+ *     events.
  *   - Return value 0 (MO_OK) or a negative MO_ERR_* code.  Argument errors are
  *     found on the host before anything is launched; mo_last_error() then returns
  *     a message (thread-local).  Faults inside kernels surface at the caller's

@@ -1,8 +1,8 @@
 // libmatopt: host side of the C ABI declared in include/matopt.h.
 //
-// One batched call = one descriptor table (uploaded to the head of the caller's
-// workspace through a pinned staging ring) + a fixed launch sequence on the
-// caller's stream:
+// One batched call = one descriptor table (written to the head of the caller's
+// workspace by copy kernels that take it as kernel arguments) + a fixed launch
+// sequence on the caller's stream:
 //   k_momentum_prep    momentum fma in place, the unscaled oriented operand X,
 //                      per-tile sum of squares                          (HBM)
 //   k_norm_scale       per-matrix s = 1 / (||M||_F + eps)                (tiny)
@@ -46,9 +46,12 @@ static __device__ __attribute__((aligned(256))) unsigned char scratch[MO_NOALLOC
 
 namespace {
 
-// Descriptor upload through kernel arguments, DESC_ARG descriptors per launch: the
-// runtime copies the argument block into its own kernel-argument memory, so this
-// needs no pinned staging buffer, no host wait and no allocation.
+// Descriptor upload through kernel arguments, DESC_ARG descriptors per launch of a
+// copy kernel into the head of the workspace: the runtime copies the argument block
+// into its own kernel-argument memory, so the upload needs no pinned staging
+// buffer, no host wait and no allocation, and stays in stream order.  (It replaced a
+// pinned staging ring with hipMemcpyAsync, which allocated on first use and made the
+// host wait once four calls were in flight; step times are unchanged.)
 constexpr int DESC_ARG = 16;
 struct DescArg {
   MatDesc d[DESC_ARG];
@@ -180,44 +183,6 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
   for (int kd = 0; kd < NKIND; ++kd)
     if (plan.total[kd] > 0x7fffffffLL) return fail(MO_ERR_INVALID, "batch too large for one launch");
   plan.bytes = off;
-  return MO_OK;
-}
-
-// ---- pinned staging ring for descriptor uploads --------------------------------
-struct StagingSlot {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
-};
-std::mutex g_stage_mu;
-StagingSlot g_ring[4];
-int g_ring_next = 0;
-
-int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  std::lock_guard<std::mutex> lock(g_stage_mu);
-  StagingSlot& s = g_ring[g_ring_next];
-  g_ring_next = (g_ring_next + 1) % 4;
-  if (s.pending) {
-    if (hipEventSynchronize(s.ev) != hipSuccess) return fail(MO_ERR_HIP, "staging event wait failed");
-    s.pending = false;
-  }
-  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
-    return fail(MO_ERR_HIP, "hipEventCreate failed");
-  if (s.cap < bytes) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    const size_t cap = std::max<size_t>(align_up(bytes, 4096), 65536);
-    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
-      return fail(MO_ERR_HIP, "hipHostMalloc of the staging buffer failed");
-    s.cap = cap;
-  }
-  std::memcpy(s.host, src, bytes);
-  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return fail(MO_ERR_HIP, "descriptor upload failed");
-  if (hipEventRecord(s.ev, stream) != hipSuccess) return fail(MO_ERR_HIP, "hipEventRecord failed");
-  s.pending = true;
   return MO_OK;
 }
 
@@ -490,11 +455,7 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   sc.redo = reinterpret_cast<int*>(sc.first + count);
   sc.partial = reinterpret_cast<double*>(base + full.off_partial);
   const NoEvents quiet(noalloc);
-  if (noalloc) {
-    MO_TRY(upload_by_args(dd, full.descs.data(), count, stream));
-  } else {
-    MO_TRY(upload(dd, full.descs.data(), sizeof(MatDesc) * count, stream));
-  }
+  MO_TRY(upload_by_args(dd, full.descs.data(), count, stream));
   if (in_dtype == MO_BF16)
     return dispatch_compute_out<bf16_t>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
   return dispatch_compute_out<float>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
