@@ -5,7 +5,7 @@
 One step = one muon_step_batched call over the whole owner set (momentum, Frobenius
 scaling, k Newton-Schulz iterations on every matrix), inputs resident in HBM.  The
 sign-vote workload's step is ns_orthogonalize over the 8 worker momenta followed by
-sign_pack per worker and one sign_vote.
+one sign_pack_batched over the 8 workers and one sign_vote.
 
 Prints ONE JSON line: matrix params/s (value), achieved TFLOP/s and % of the dense
 MFMA peak of the compute dtype, a per-kernel breakdown from HIP events recorded by
@@ -236,17 +236,19 @@ class Run:
         self.ws = ws
         if wid == 5:
             moms = [device_matrix(5, i, dev)[1] for i in range(w.count)]
-            outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
-            nwords = (shapes[0][0] * shapes[0][1] + 31) // 32
+            # the workers' directions side by side, so one launch packs them all
+            stack = torch.empty((w.count,) + tuple(shapes[0]), dtype=torch.bfloat16, device=dev)
+            outs = [stack[i] for i in range(w.count)]
+            numel = shapes[0][0] * shapes[0][1]
+            nwords = (numel + 31) // 32
             packed = torch.empty((w.count, nwords), dtype=torch.int32, device=dev)
             vote = torch.empty(nwords, dtype=torch.int32, device=dev)
-            self.tensors = [moms, outs, packed, vote]
+            self.tensors = [moms, stack, packed, vote]
 
             def step():
                 mo.ns_orthogonalize(moms, outs, *MUON_ABC, w.iters, EPS, compute=compute, workspace=ws)
-                for i in range(w.count):
-                    mo.sign_pack(outs[i], packed[i])
-                mo.sign_vote(packed, outs[0].numel(), out_packed=vote)
+                mo.sign_pack_batched(stack.view(w.count, numel), packed)
+                mo.sign_vote(packed, numel, out_packed=vote)
         else:
             grads, moms = [], []
             for i in range(w.count):

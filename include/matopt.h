@@ -147,6 +147,16 @@ int32_t ns_orthogonalize(const mo_matrix *mats, int32_t count, int32_t in_dtype,
  * pad bits 0).  numel >= 1. */
 int32_t sign_pack(const void *u, int32_t dtype, int64_t numel, uint32_t *packed, void *stream);
 
+/* sign_pack for M workers in one launch ("Riepilogo Tecnico: SignMuon", section 2,
+ * core mechanism item 2 and distributed flow items 2-3: every worker packs the signs
+ * of its own direction).  Worker w's numel values (dtype MO_F32 or MO_BF16) start at
+ * element w * u_stride of u (u_stride >= numel when M > 1; ignored when M == 1); its
+ * ceil(numel/32) words go to packed + w * ceil(numel/32), so packed receives the
+ * [M][ceil(numel/32)] stack sign_vote reads.  Same bits as M calls of sign_pack.
+ * 1 <= M <= 65535, numel >= 1. */
+int32_t sign_pack_batched(const void *u, int32_t dtype, int32_t M, int64_t numel, int64_t u_stride,
+                          uint32_t *packed, void *stream);
+
 /* Majority vote over M packed sign buffers ("Riepilogo Tecnico: SignMuon",
  * section 2, core mechanism item 3 and distributed flow item 4: integer sum of the
  * signs, then a sign threshold).  packed: [M][ceil(numel/32)] uint32, worker-major

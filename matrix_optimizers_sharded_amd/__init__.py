@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     muon_step_apply,
     ns_orthogonalize,
     sign_pack,
+    sign_pack_batched,
     sign_vote,
     sign_unpack,
     sign_apply,

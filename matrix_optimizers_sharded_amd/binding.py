@@ -62,6 +62,8 @@ def load_library():
     lib.ns_orthogonalize.restype = I32
     lib.sign_pack.argtypes = [P, I32, I64, P, P]
     lib.sign_pack.restype = I32
+    lib.sign_pack_batched.argtypes = [P, I32, I32, I64, I64, P, P]
+    lib.sign_pack_batched.restype = I32
     lib.sign_vote.argtypes = [P, I32, I64, P, P, P]
     lib.sign_vote.restype = I32
     lib.muon_step_batched_noalloc.argtypes = [ctypes.POINTER(MoMatrix), I32, I32, I32, I32, F,
@@ -322,6 +324,25 @@ def sign_pack(u, packed=None):
         raise MatoptError(-1, "packed must be a contiguous int32 tensor of ceil(numel/32) words")
     with _on(_one_device(u, packed)):
         _check(lib.sign_pack(u.data_ptr(), _dtype_code(u.dtype), numel, packed.data_ptr(), _stream_ptr(u)))
+    return packed
+
+
+def sign_pack_batched(u, packed=None):
+    """1-bit signs of each row of u (M x numel, unit column stride; rows may be
+    padded) -> int32 tensor [M][ceil(numel/32)], the stack sign_vote takes."""
+    import torch
+    lib = load_library()
+    if not u.is_cuda or u.dim() != 2 or u.stride(1) != 1 or (u.shape[0] > 1 and u.stride(0) < u.shape[1]):
+        raise MatoptError(-1, "u must be a CUDA tensor [M][numel] with contiguous rows")
+    M, numel = u.shape
+    nwords = (numel + 31) // 32
+    if packed is None:
+        packed = torch.empty((M, nwords), dtype=torch.int32, device=u.device)
+    if packed.dtype != torch.int32 or not packed.is_contiguous() or tuple(packed.shape) != (M, nwords):
+        raise MatoptError(-1, "packed must be a contiguous int32 tensor [M][ceil(numel/32)]")
+    with _on(_one_device(u, packed)):
+        _check(lib.sign_pack_batched(u.data_ptr(), _dtype_code(u.dtype), M, numel, u.stride(0), packed.data_ptr(),
+                                     _stream_ptr(u)))
     return packed
 
 

@@ -385,11 +385,17 @@ __device__ inline uint32_t sign_byte(const T* __restrict__ u, int64_t e0, int64_
 
 // One thread per 8 consecutive elements of each unit -> one byte; 4 lanes OR their
 // bytes into a 32-bit word (element i -> bit i % 32 of word i / 32).  bit = (u >= 0).
+// Row y of the grid packs worker y: its numel values start at u + y * u_stride and
+// its words at packed + y * nwords (the [M][nwords] stack a vote reads), so M
+// workers take one launch.  (A grid of a few blocks per CU looping over the bytes,
+// four per thread per round, was slower at 2^28 elements: 3.98 against 4.71 TB/s.)
 template <typename T>
-__global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int64_t numel,
+__global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int64_t u_stride, int64_t numel,
                                                    uint32_t* __restrict__ packed, int vec_ok) {
   const int lane = threadIdx.x & 63;
   const int64_t nwords = (numel + 31) >> 5;
+  u += static_cast<int64_t>(blockIdx.y) * u_stride;
+  packed += static_cast<int64_t>(blockIdx.y) * nwords;
   uint32_t bytes[PACK_UNITS];
 #pragma unroll
   for (int s = 0; s < PACK_UNITS; ++s) {

@@ -502,24 +502,33 @@ int32_t ns_orthogonalize(const mo_matrix* mats, int32_t count, int32_t in_dtype,
                  stream);
 }
 
-int32_t sign_pack(const void* u, int32_t dtype, int64_t numel, uint32_t* packed, void* stream_ptr) {
+int32_t sign_pack_batched(const void* u, int32_t dtype, int32_t M, int64_t numel, int64_t u_stride,
+                          uint32_t* packed, void* stream_ptr) {
   g_err.clear();
   if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
+  if (M < 1 || M > 65535) return fail(MO_ERR_INVALID, "M must be in [1, 65535]");
+  if (M > 1 && u_stride < numel) return fail(MO_ERR_INVALID, "u_stride must be >= numel when M > 1");
   if (!u || !packed) return fail(MO_ERR_INVALID, "u or packed is NULL");
   const int64_t threads = ((numel + 31) / 32) * 4;
   const int64_t blocks = (threads + 256 * PACK_UNITS - 1) / (256 * PACK_UNITS);
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const int vec = aligned16(u) ? 1 : 0;
+  // 16-byte loads when every worker's values start 16-byte aligned
+  const int64_t stride = M > 1 ? u_stride : 0;
+  const int vec = (aligned16(u) && (static_cast<uint64_t>(stride) * dtype_size(dtype)) % 16 == 0) ? 1 : 0;
   return launch(PK_PACK, stream, [&] {
     if (dtype == MO_F32)
-      hipLaunchKernelGGL((k_sign_pack<float>), dim3(blocks), dim3(256), 0, stream,
-                         static_cast<const float*>(u), numel, packed, vec);
+      hipLaunchKernelGGL((k_sign_pack<float>), dim3(blocks, M), dim3(256), 0, stream, static_cast<const float*>(u),
+                         stride, numel, packed, vec);
     else
-      hipLaunchKernelGGL((k_sign_pack<bf16_t>), dim3(blocks), dim3(256), 0, stream,
-                         static_cast<const bf16_t*>(u), numel, packed, vec);
+      hipLaunchKernelGGL((k_sign_pack<bf16_t>), dim3(blocks, M), dim3(256), 0, stream,
+                         static_cast<const bf16_t*>(u), stride, numel, packed, vec);
   });
+}
+
+int32_t sign_pack(const void* u, int32_t dtype, int64_t numel, uint32_t* packed, void* stream_ptr) {
+  return sign_pack_batched(u, dtype, 1, numel, numel, packed, stream_ptr);
 }
 
 int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* out_packed, int8_t* out_sum,

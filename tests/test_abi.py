@@ -156,3 +156,14 @@ def test_noalloc_rejects_lists_beyond_its_scratch_on_the_host(lib):
     text = open(HEADER).read()
     assert re.search(r"#define MO_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", text)
     assert binding.NOALLOC_SCRATCH_BYTES == 256 << 20
+
+
+def test_sign_pack_batched_validates_on_the_host(lib):
+    fake = ctypes.c_void_p(0x1000)
+    out = ctypes.c_void_p(0x2000)
+    assert lib.sign_pack_batched(fake, 0, 0, 64, 64, out, None) == -1            # M < 1
+    assert lib.sign_pack_batched(fake, 0, 2, 64, 63, out, None) == -1            # rows overlap
+    assert b"u_stride" in lib.mo_last_error()
+    assert lib.sign_pack_batched(fake, 0, 2, 0, 64, out, None) == -1             # numel < 1
+    assert lib.sign_pack_batched(None, 0, 2, 64, 64, out, None) == -1            # null input
+    assert lib.sign_pack_batched(fake, 5, 2, 64, 64, out, None) == -2            # dtype

@@ -59,6 +59,33 @@ def test_sign_pack_unaligned_view(gpu):
     np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), oracle.sign_pack(v[1:]))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,numel,pad", [(1, 33, 0), (3, 1, 0), (3, 31, 5), (8, 1000, 0), (8, 1000, 3),
+                                         (5, 65537, 0), (2, 4096, 4)])
+def test_sign_pack_batched_bit_exact(gpu, dtype, M, numel, pad):
+    """One launch over M workers (rows of u, each row padded by pad values) gives
+    each worker's words, bit for bit, in the [M][nwords] stack."""
+    import torch
+    from matrix_optimizers_sharded_amd import sign_pack_batched
+    say(f"sign_pack_batched dtype={dtype} M={M} numel={numel} pad={pad}")
+    rng = np.random.default_rng(M * 1000 + numel + pad)
+    v = rng.standard_normal((M, numel + pad)).astype(np.float32)
+    v[rng.random(v.shape) < 0.05] = 0.0
+    v[rng.random(v.shape) < 0.05] = -0.0
+    if dtype == "bf16":
+        bits, vals = bf16_round(v)
+        full = to_dev_bf16(bits, gpu)
+    else:
+        full = to_dev_f32(v, gpu)
+    u = full[:, :numel]
+    packed = sign_pack_batched(u)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy().view(np.uint32)
+    host = host_f32(full)
+    for w in range(M):
+        np.testing.assert_array_equal(got[w], oracle.sign_pack(host[w, :numel]), err_msg=f"worker {w}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 15, 16, 127])
 @pytest.mark.parametrize("numel", [1, 33, 1000, 65537])
 def test_sign_vote_bit_exact(gpu, M, numel):
