@@ -21,7 +21,9 @@ enum Kind {
   KIND_APPLY = 2,  // 256x256 tiles of X <- aX + BX
   KIND_PREP = 3,   // 64x64 tiles of the padded oriented X0 (and X0^T)
   KIND_CHUNK = 4,  // 4096-element chunks of the caller's matrix (momentum, norm)
-  NKIND = 5
+  KIND_SMALL_UPPER = 5,   // upper-triangle 32x32 blocks of A or B (calls on the small path)
+  KIND_SMALL_RECT = 6,    // 32x32 blocks of X (small path)
+  NKIND = 7
 };
 
 constexpr int GEMM_TILE = 256;   // workspace dims are padded to multiples of this
@@ -57,7 +59,9 @@ struct MatDesc {
   int32_t transposed;     // 1 if rows > cols (X = M^T)
   int32_t vec_ok;         // 1 if grad/mom/out allow 16-byte vector access
   // workspace buffers, compute dtype, k-blocked (see kb_off), zero outside the m x n
-  // corner
+  // corner: the first pass writes all of X; the products write their padding as
+  // exact zeros, on the 256-tile path up to mp / np and on the small path up to the
+  // next multiple of 32, which is as far as that path reads
   void* X[2];             // mp x np (k = column), ping-pong: iteration t reads X[t % 2]
                           // (SYRK's operands, APPLY's second operand) and APPLY writes
                           // X[(t + 1) % 2]

@@ -33,6 +33,7 @@
 #include "common.h"
 #include "elementwise.h"
 #include "gemm.h"
+#include "smallgemm.h"
 #include "planner.h"
 
 using namespace mo;
@@ -84,7 +85,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Plan {
   std::vector<MatDesc> descs;
-  int64_t total[NKIND] = {0, 0, 0, 0, 0};
+  int64_t total[NKIND] = {};
   size_t off_desc = 0, off_scale = 0, off_partial = 0, bytes = 0;
 };
 // The per-matrix scalars at off_scale: scale[count] (s = 1 / (||M||_F + eps)),
@@ -169,10 +170,16 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.X[1] = take(xb);
     d.A = take(ab);
     d.B = take(ab);
+    // products: matrices with m <= 256 on 32 x 32 blocks (smallgemm.h), the others
+    // on 256 x 256 tiles; the choice depends on the matrix alone, so a matrix's
+    // result never depends on the rest of the batch
+    const bool small = d.mp == GEMM_TILE;
     const int64_t tm = d.mp / GEMM_TILE, tn = d.np / GEMM_TILE;
-    d.items[KIND_SYRK] = tm * (tm + 1) / 2;
-    d.items[KIND_POLY] = tm * (tm + 1) / 2;
-    d.items[KIND_APPLY] = tm * tn;
+    d.items[KIND_SYRK] = small ? 0 : tm * (tm + 1) / 2;
+    d.items[KIND_POLY] = small ? 0 : tm * (tm + 1) / 2;
+    d.items[KIND_APPLY] = small ? 0 : tm * tn;
+    d.items[KIND_SMALL_UPPER] = small ? small_upper_items(d.m) : 0;
+    d.items[KIND_SMALL_RECT] = small ? small_rect_items(d.m, d.n) : 0;
     d.items[KIND_PREP] = (int64_t(d.mp) / PREP_TILE) * (int64_t(d.np) / PREP_TILE);
     d.items[KIND_CHUNK] = (d.numel + CHUNK - 1) / CHUNK;
     for (int kd = 0; kd < NKIND; ++kd) {
@@ -268,33 +275,62 @@ struct ApplyOpt {
   float lr = 0.f;
 };
 
+// k NS iterations: per product one persistent 256 x 256-tile launch over the
+// matrices with m > 256 and one 32 x 32-block launch (smallgemm.h) over those with
+// m <= 256; a launch with no items is skipped.
 template <typename T, typename TO>
 int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
            const float* first, hipStream_t stream) {
-  const int64_t gs = gemm_grid(plan.total[KIND_SYRK]), ga = gemm_grid(plan.total[KIND_APPLY]);
+  const int64_t ts = plan.total[KIND_SYRK], ta = plan.total[KIND_APPLY];
+  const int64_t nu = plan.total[KIND_SMALL_UPPER], nr = plan.total[KIND_SMALL_RECT];
+  const int64_t gs = gemm_grid(ts), ga = gemm_grid(ta);
+  const dim3 gu((nu + 3) / 4), gr((nr + 3) / 4);
   for (int t = 0; t < ns.iters; ++t) {
     const int parity = t & 1;
     const float* f = t == 0 ? first : nullptr;   // the Frobenius factor, first iteration only
-    MO_TRY(launch(PK_SYRK, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                         dd, count, plan.total[KIND_SYRK], parity, 0.f, 0.f, 0.f, f);
-    }));
-    MO_TRY(launch(PK_POLY, stream, [&] {
-      hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                         dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c, nullptr);
-    }));
     const bool last = (t + 1 == ns.iters);
-    MO_TRY(launch(PK_APPLY, stream, [&] {
-      if (last && ap.on)
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, ap.lr, 0.f, 0.f, f);
-      else if (last)
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f, f);
-      else
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_APPLY], parity, 0.f, 0.f, 0.f, f);
-    }));
+    if (ts > 0) {
+      MO_TRY(launch(PK_SYRK, stream, [&] {
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
+                           dd, count, ts, parity, 0.f, 0.f, 0.f, f);
+      }));
+      MO_TRY(launch(PK_POLY, stream, [&] {
+        hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
+                           dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c, nullptr);
+      }));
+      MO_TRY(launch(PK_APPLY, stream, [&] {
+        if (last && ap.on)
+          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                             dd, count, ta, parity, ap.lr, 0.f, 0.f, f);
+        else if (last)
+          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                             dd, count, ta, parity, 0.f, 0.f, 0.f, f);
+        else
+          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
+                             dd, count, ta, parity, 0.f, 0.f, 0.f, f);
+      }));
+    }
+    if (nu > 0) {
+      MO_TRY(launch(PK_SYRK, stream, [&] {
+        hipLaunchKernelGGL((k_ns_small<T, GM_SYRK, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, 0.f,
+                           0.f, 0.f, f);
+      }));
+      MO_TRY(launch(PK_POLY, stream, [&] {
+        hipLaunchKernelGGL((k_ns_small<T, GM_POLY, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, ns.a,
+                           ns.b, ns.c, nullptr);
+      }));
+      MO_TRY(launch(PK_APPLY, stream, [&] {
+        if (last && ap.on)
+          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_WEIGHT, TO>), gr, dim3(256), 0, stream, dd, count, nr,
+                             parity, ap.lr, 0.f, 0.f, f);
+        else if (last)
+          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_FINAL, TO>), gr, dim3(256), 0, stream, dd, count, nr,
+                             parity, 0.f, 0.f, 0.f, f);
+        else
+          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY, TO>), gr, dim3(256), 0, stream, dd, count, nr, parity,
+                             0.f, 0.f, 0.f, f);
+      }));
+    }
   }
   return MO_OK;
 }

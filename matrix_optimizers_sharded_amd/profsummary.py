@@ -25,9 +25,9 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 KINDS = [
-    (re.compile(r"k_ns_gemm.*Li0E"), "ns_syrk"),
-    (re.compile(r"k_ns_gemm.*Li1E"), "ns_poly"),
-    (re.compile(r"k_ns_gemm.*Li[234]E"), "ns_apply"),
+    (re.compile(r"k_ns_(gemm|small).*Li0E"), "ns_syrk"),
+    (re.compile(r"k_ns_(gemm|small).*Li1E"), "ns_poly"),
+    (re.compile(r"k_ns_(gemm|small).*Li[234]E"), "ns_apply"),
     (re.compile(r"k_momentum_sumsq"), "momentum_sumsq"),
     (re.compile(r"k_momentum_prep"), "momentum_prep"),
     (re.compile(r"k_prep_redo"), "prep_operand"),

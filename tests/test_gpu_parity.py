@@ -164,12 +164,16 @@ def test_single_256x128_fp32(gpu):
 
 
 RAGGED = [(1, 1), (1, 300), (300, 1), (257, 129), (129, 257), (300, 200), (512, 512), (700, 260), (64, 1000)]
+# Matrices with min(rows, cols) <= 256 run their products on 32 x 32 blocks, one wave
+# each; larger ones on the persistent 256 x 256 tiles.  RAGGED holds both kinds.
+SMALL_M = 256
 
 
 @pytest.mark.parametrize("compute", ["f32", "bf16"])
 @pytest.mark.parametrize("iters", [0, 1, 5])
 def test_ragged_shapes(gpu, compute, iters):
     import torch
+    assert any(min(s) <= SMALL_M for s in RAGGED) and any(min(s) > SMALL_M for s in RAGGED)
     say(f"ragged shapes compute={compute} iters={iters}")
     grads = [gaussian(s, 100 + i) for i, s in enumerate(RAGGED)]
     moms = [gaussian(s, 200 + i) for i, s in enumerate(RAGGED)]
@@ -225,9 +229,10 @@ def test_zero_matrix_gives_zero(gpu):
 def test_extreme_input_scales(gpu, scale):
     """Inputs near the fp32 range ends: at 2^70 the squares (2^140) overflow fp32, so
     the Frobenius sum must not be formed in fp32; at 2^-70 the norm falls far below
-    eps and X0 = x / (|x|_F + eps) stays tiny.  Both must follow the oracle."""
+    eps and X0 = x / (|x|_F + eps) stays tiny.  Both must follow the oracle, on both
+    product paths (m = 300 on 256 x 256 tiles, m = 200 on 32 x 32 blocks)."""
     import torch
-    shapes = [(300, 520), (520, 300)]
+    shapes = [(300, 520), (520, 300), (200, 520), (520, 200)]
     xs = [(gaussian(s, 700 + i) * np.float32(scale)).astype(np.float32) for i, s in enumerate(shapes)]
     assert all(np.isfinite(x).all() for x in xs)
     say(f"extreme scale 2^{int(np.log2(scale))}")
@@ -244,13 +249,17 @@ def test_first_product_scaling_range(gpu):
     Frobenius factor, unless the norm lies outside [2^-20, 2^40]; then the operand is
     rewritten scaled.  One batch holds matrices just inside and just outside both
     ends (norms about 2^-19.4, 2^-21.4, 2^39.6, 2^40.6), so both routes run side by
-    side in one call and each must follow the oracle."""
+    side in one call and each must follow the oracle, on both product paths (m = 300
+    on 256 x 256 tiles, m = 200 on 32 x 32 blocks)."""
     import torch
     shapes = [(300, 520), (520, 300), (300, 520), (520, 300)]
     exps = [-28, -30, 31, 32]   # the unit Gaussians have norm about 2^8.6
+    shapes = shapes + [(200, 520), (520, 200), (200, 520), (520, 200)]
+    exps = exps + [-28, -30, 31, 32]
     xs = [(gaussian(s, 720 + i) * np.float32(2.0 ** e)).astype(np.float32) for i, (s, e) in enumerate(zip(shapes, exps))]
     norms = [np.log2(np.linalg.norm(x.astype(np.float64))) for x in xs]
-    assert norms[0] > -20 > norms[1] and norms[2] < 40 < norms[3], norms
+    for q in (0, 4):
+        assert norms[q] > -20 > norms[q + 1] and norms[q + 2] < 40 < norms[q + 3], norms
     say(f"first-product scaling, log2 norms {[round(v, 2) for v in norms]}")
     for compute in ("f32", "bf16"):
         got = run_ns(gpu, xs, tdt("f32"), tdt(compute), tdt("f32"), MUON_ABC, 5, EPS)
