@@ -12,6 +12,7 @@ import gc
 
 import numpy as np
 import pytest
+import scipy.linalg
 
 import oracle
 from matrix_optimizers_sharded_amd.workloads import (
@@ -63,12 +64,64 @@ def run_owner_set(gpu, wid, sample):
     return w, grads, moms, outs, host
 
 
-def check_owner_set(wid, sample, gpu):
+def gram_singular_values(x):
+    """Singular values of a wide or tall float64 matrix from the eigenvalues of its
+    smaller Gram matrix (ascending).  Their absolute error is about
+    eps * sigma_max^2 / sigma, far below the tolerances they are compared with."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x @ x.T if x.shape[0] <= x.shape[1] else x.T @ x
+    ev = scipy.linalg.eigvalsh(g, check_finite=False)
+    return np.sqrt(np.clip(ev, 0.0, None))
+
+
+def spectral_norm_exact(x):
+    x = np.asarray(x, dtype=np.float64)
+    g = x @ x.T if x.shape[0] <= x.shape[1] else x.T @ x
+    top = scipy.linalg.eigvalsh(g, subset_by_index=[g.shape[0] - 1, g.shape[0] - 1], check_finite=False)
+    return float(np.sqrt(max(top[0], 0.0)))
+
+
+# Widening of the band for the bf16 path, as a fraction of the band's top: the
+# measured spectral norm of the GPU's error is 1.2e-2 to 2.4e-2 at the 1B- and
+# 7B-class shapes (1-2% of the top, about 1.2), because bf16 operands perturb every
+# singular value by roughly the same absolute amount.  5% of the top is a wide
+# margin for that and still rejects a result scaled by 6%.  The same absolute
+# margin applies at the bottom; where sigma_min(X0) is tiny (square Gaussian
+# matrices: about 5e-6, a band bottom near 3e-3) the bottom lies below the
+# rounding level and only the top binds.
+BAND_TOL = 0.05
+
+
+def check_spectrum(label, d, u_gpu, u_or, iters):
+    """Both ends of the spectrum of the GPU's U against the band the iteration
+    implies: exact NS maps each singular value sigma of X0 to p^k(sigma) (p(s) = a s
+    + b s^3 + c s^5), so the singular values of U lie in [min, max] of p^k over the
+    actual singular values of X0 (the lower end from the actual sigma_min).  The
+    GPU's must lie in that band widened by BAND_TOL of its top at each end.  As a check of the
+    computation itself, each singular value of U_gpu is also within
+    ||U_gpu - U_oracle||_2 of its exact image (Weyl's inequality)."""
+    x0 = oracle.frobenius_normalize(oracle.momentum_update(d["grad"], d["mom"], BETA), EPS)
+    s0 = gram_singular_values(x0)
+    want = np.sort(np.abs(scalar_poly_iterate(s0, *MUON_ABC, iters)))
+    got = gram_singular_values(u_gpu)
+    delta = spectral_norm_exact(u_gpu - u_or)
+    lo, hi = float(want[0]), float(want[-1])
+    say(f"{label}: sigma(X0) in [{s0[0]:.3e}, {s0[-1]:.3e}]; band [{lo:.4f}, {hi:.4f}]; "
+        f"sigma(U_gpu) in [{got[0]:.4f}, {got[-1]:.4f}]; ||dU||_2 = {delta:.3e}")
+    margin = BAND_TOL * hi
+    assert got[-1] <= hi + margin, f"{label}: sigma_max {got[-1]:.5f} above the band top {hi:.5f}"
+    assert got[0] >= lo - margin, f"{label}: sigma_min {got[0]:.5f} below the band bottom {lo:.5f}"
+    assert float(np.max(np.abs(got - want))) <= delta + 1e-9, f"{label}: singular values inconsistent"
+
+
+def check_owner_set(wid, sample, gpu, spectrum):
     import torch
     w, grads, moms, outs, host = run_owner_set(gpu, wid, sample)
     top = band_top(MUON_ABC, w.iters)
     for i, u in enumerate(outs):
         assert bool(torch.isfinite(u.float()).all()), f"matrix {i} not finite"
+    # every sixteenth matrix: a lower bound on sigma_max against the band's top for
+    # any sigma in [0, 1] (no host copy of those inputs exists)
     for i in range(0, w.count, max(1, w.count // 16)):
         s = spectral_norm(outs[i])
         assert s <= top * 1.02 + 1e-3, f"matrix {i}: sigma_max {s:.4f} above the band top {top:.4f}"
@@ -77,9 +130,12 @@ def check_owner_set(wid, sample, gpu):
         say(f"{w.name}: oracle on matrix {i} {d['shape']}")
         want_m, want_u = oracle.muon_step(d["grad"], d["mom"], BETA, *MUON_ABC, w.iters, EPS)
         np.testing.assert_array_equal(host_f32(moms[i]).view(np.uint32), want_m.view(np.uint32))
-        e = rel_err(host_f32(outs[i]), want_u)
+        u_gpu = host_f32(outs[i])
+        e = rel_err(u_gpu, want_u)
         say(f"{w.name}: matrix {i} rel err {e:.3e}")
         assert e <= 2e-2, (i, e)
+        if i in spectrum:
+            check_spectrum(f"{w.name} matrix {i}", d, u_gpu, want_u, w.iters)
     del grads, moms, outs
     gc.collect()
     torch.cuda.empty_cache()
@@ -88,13 +144,13 @@ def check_owner_set(wid, sample, gpu):
 @pytest.mark.timeout(900)
 def test_1b_class_swiglu_heavy_tailed(gpu):
     # one of each shape (2048^2, 2048x5632, 5632x2048) from the first and last layer
-    check_owner_set(3, [0, 4, 6, 105, 111], gpu)
+    check_owner_set(3, [0, 4, 6, 105, 111], gpu, spectrum=[0, 4, 6, 105, 111])
 
 
 @pytest.mark.timeout(1200)
 def test_7b_class_owner_set(gpu):
     # 4096^2, 4096x11008, 11008x4096 from layer 0, and the last matrix of layer 31
-    check_owner_set(4, [0, 4, 6, 223], gpu)
+    check_owner_set(4, [0, 4, 6, 223], gpu, spectrum=[0, 6])
 
 
 @pytest.mark.timeout(900)
@@ -128,7 +184,15 @@ def test_sign_muon_vote_8x4096(gpu):
         u_or = oracle.ns_orthogonalize(ins[i], *MUON_ABC, w.iters, EPS)
         e = rel_err(u_gpu[i], u_or)
         assert e <= 2e-2, (i, e)
+        # A sign can flip only where the error exceeds the oracle's value.  Flips are
+        # allowed where |U_oracle| is below 8 times the rms elementwise error.  With
+        # normal-like errors (rms about 0.9% of the values' spread) about one flip per
+        # 1.7e7-element worker is expected between 4 and 5 rms (3.8 rms measured), so
+        # a bound of 4 rms would reject faithful results by chance; beyond 8 rms the
+        # expected count is below 1e-9, so a flip there means an error spike.
         flips = (u_gpu[i] >= 0) != (u_or >= 0)
-        scale = 8.0 * np.linalg.norm(u_gpu[i] - u_or) / np.sqrt(numel)
-        say(f"worker {i}: rel err {e:.3e}, sign flips {flips.mean():.2e}")
-        assert np.all(np.abs(u_or[flips]) <= scale), "a sign flipped where the oracle value is large"
+        rms = np.linalg.norm(u_gpu[i] - u_or) / np.sqrt(numel)
+        worst = float(np.max(np.abs(u_or[flips]))) / rms if flips.any() else 0.0
+        say(f"worker {i}: rel err {e:.3e}, sign flips {flips.mean():.2e}, largest |U_oracle| at a flip "
+            f"{worst:.2f} rms")
+        assert worst <= 8.0, "a sign flipped where the oracle value is large"
