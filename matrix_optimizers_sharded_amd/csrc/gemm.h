@@ -52,16 +52,9 @@ constexpr int GT = GEMM_TILE;          // 256
 // only by the next launch, so they need not displace the operand panels that the
 // other blocks of an XCD are sharing in L2.  Measured: -0.5% time for the staged
 // whole-line transposed copies, a further -1.1% for the row-major results.
-#ifndef MO_GEMM_NT_STORES
-#define MO_GEMM_NT_STORES 1
-#endif
 template <typename V>
 __device__ inline void store_ws(gptr<V> p, const V& v) {
-#if MO_GEMM_NT_STORES
   __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 constexpr int ROW_BYTES = KB_BYTES;
 constexpr int CHUNKS = ROW_BYTES / 16;                 // 16-byte chunks per row
@@ -187,13 +180,7 @@ template <> struct Mfma<float> {
 // band is walked column by column, top to bottom within a column.  Consecutive
 // items (which run at the same time on one XCD) then form a BAND x 8 block whose
 // operand row-panels are shared through that XCD's L2.
-#ifndef MO_GEMM_BAND
-#define MO_GEMM_BAND 4
-#endif
-#ifndef MO_GEMM_XCD_REMAP
-#define MO_GEMM_XCD_REMAP 1
-#endif
-constexpr int BAND = MO_GEMM_BAND;
+constexpr int BAND = 4;
 
 __device__ inline void rect_tile(int64_t local, int tm, int tn, int& ti, int& tj) {
   const int64_t per_band = static_cast<int64_t>(BAND) * tn;
@@ -230,15 +217,12 @@ __device__ inline void upper_tile(int64_t local, int T, int& ti, int& tj) {
 }
 
 // Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  Remap so that
-// XCD x receives runs of XCD_CHUNK consecutive work items (chunks dealt round-robin
+// XCD x receives runs of G = 32 consecutive work items (chunks dealt round-robin
 // over the XCDs): the blocks one XCD runs at a time are neighbours in the work
 // list and share operand panels in that XCD's L2, while all XCDs still progress
 // through the list together (equal load).
-#ifndef MO_GEMM_XCD_CHUNK
-#define MO_GEMM_XCD_CHUNK 32
-#endif
 __device__ inline int64_t xcd_remap(int64_t b, int64_t total) {
-  constexpr int64_t G = MO_GEMM_XCD_CHUNK;
+  constexpr int64_t G = 32;
   const int64_t full = total / (8 * G) * (8 * G);   // blocks in complete rounds
   if (b >= full) return b;                          // ragged tail: identity
   const int64_t x = b % 8, k = b / 8;               // k-th block of XCD x
@@ -404,7 +388,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   const uint32_t qlane = static_cast<uint32_t>(qrow) * ROW_BYTES + (((lane % 8) ^ swz_tr(qrow)) << 4);
 
   auto setup = [&](int64_t v, TileRef& t) {
-    const int64_t item = MO_GEMM_XCD_REMAP ? xcd_remap(v, total) : v;
+    const int64_t item = xcd_remap(v, total);
     const int di = __builtin_amdgcn_readfirstlane(find_desc(descs, count, kind, item));
     const MatDesc* d = descs + di;
     const int64_t local = item - d->begin[kind];
@@ -460,10 +444,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // a full texture-address FIFO.  Measured at the 7B-class set: 4 loaders -4% per
   // step against 8 (APPLY -5.5%, SYRK -3%, POLY unchanged).  fp32 operands keep all
   // 8 waves loading (their APPLY slab maps wave w + 4 to another k-block).
-#ifndef MO_GEMM_LOADERS
-#define MO_GEMM_LOADERS 4
-#endif
-  constexpr int LOADERS = sizeof(T) == 2 ? MO_GEMM_LOADERS : NWAVES;
+  constexpr int LOADERS = sizeof(T) == 2 ? 4 : NWAVES;
   static_assert(NWAVES % LOADERS == 0 && (LOADERS == NWAVES || sizeof(T) == 2), "loader waves");
   // this wave's loads of k-block kt of one operand (h = 0: P, h = 1: Q) into a stage
   auto issue_op = [&](const TileRef& t, int kt, int stage, int h) {
