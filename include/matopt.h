@@ -31,7 +31,9 @@
  *     memory on these calls; scratch comes from the caller's `workspace` (size
  *     from muon_workspace_bytes), whose head receives the per-call descriptor
  *     table through the kernel arguments of small copy kernels.
- *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and the
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream), so that
+ *     callers need no HIP header; the Newton-Schulz parameters are passed by
+ *     pointer (read before return).  Work is enqueued and the
  *     call returns without waiting for the GPU.  `mats` is read before return.
  *     With profiling on (mo_profile_begin), calls also create and record HIP
  *     events.
@@ -84,14 +86,21 @@ typedef struct {
 } mo_matrix;
 
 /* Bytes of device workspace muon_step_batched / ns_orthogonalize need for this
- * list with this compute dtype (MO_F32 or MO_BF16).  Returns 0 if the list is
- * invalid (then mo_last_error() says why).  The workspace holds, per matrix, two
+ * list with this compute dtype (MO_F32 or MO_BF16): the scratch of the owner's local
+ * update of every whole matrix it holds ("Riassunto Tecnico: MatrixFSDP",
+ * Metodologia item 1).  Returns 0 if the list is invalid (then mo_last_error() says
+ * why).  The workspace holds, per matrix, two
  * copies of the iterate X (ping-pong), A and B, each padded to multiples of 256 in
  * both dimensions, plus the per-call descriptor table and the per-matrix norm
  * partial sums. */
 size_t muon_workspace_bytes(const mo_matrix *mats, int32_t count, int32_t compute_dtype);
 
-/* The owner-local Muon step on `count` matrices, batched: for each matrix
+/* The owner-local Muon step on `count` matrices, batched ("Riassunto Tecnico:
+ * MatrixFSDP", Metodologia item 1: the owner of a whole matrix runs the
+ * Newton-Schulz update locally; "Riepilogo Tecnico: SignMuon", section 2, core
+ * mechanism item 1 and distributed flow item 1: the local momentum update, then its
+ * Newton-Schulz polar direction; section 4, nanoGPT: Frobenius scaling).  For each
+ * matrix
  *   M <- beta*M + G            (fp32, in place)
  *   X <- M / (||M||_F + eps)   (oriented so that rows <= cols)
  *   repeat ns->iters times: A = X X^T; B = b A + c A A; X <- a X + B X
@@ -134,8 +143,11 @@ int32_t muon_step_batched_noalloc(const mo_matrix *mats, int32_t count, int32_t 
                                   int32_t compute_dtype, int32_t out_dtype, float beta,
                                   const mo_ns_params *ns, void *stream);
 
-/* Frobenius scaling and Newton-Schulz only (no momentum): out <- NS(x / (||x|| + eps)).
- * in_dtype: MO_F32 or MO_BF16.  x == out is allowed. */
+/* Frobenius scaling and Newton-Schulz only (no momentum): out <- NS(x / (||x|| + eps))
+ * ("Riepilogo Tecnico: SignMuon", section 2, core mechanism item 1: the polar
+ * direction of a worker's momentum; Flusso Algoritmico item 5: the optional polar
+ * step on the voted signs).  in_dtype: MO_F32 or MO_BF16.  x == out is allowed.
+ * Same arguments, conventions and workspace as muon_step_batched otherwise. */
 int32_t ns_orthogonalize(const mo_matrix *mats, int32_t count, int32_t in_dtype,
                          int32_t compute_dtype, int32_t out_dtype, const mo_ns_params *ns,
                          void *workspace, size_t workspace_bytes, void *stream);
