@@ -162,6 +162,29 @@ def blas_ceiling(torch, dev, seconds=2.0):
     return out
 
 
+def copy_ceiling(torch, dev, nbytes=4 << 30, reps=20):
+    """What a plain device-to-device copy (torch's copy kernel) moves on this GPU, read
+    plus write bytes per second: the practical ceiling for the streaming kernels,
+    which read and write in a similar mix."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms / 1e3) / 1e9
+    print(f"[bench] device copy of {nbytes >> 20} MiB: {ms:.3f} ms, {gbs:.0f} GB/s read+write", file=sys.stderr,
+          flush=True)
+    del src, dst
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_info():
     """CPU model, logical core count and the BLAS library numpy calls (name, version,
     threads) on this host."""
@@ -375,7 +398,8 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.blas_only:
-        print(json.dumps({"blas_ceiling": blas_ceiling(torch, dev)}), flush=True)
+        print(json.dumps({"blas_ceiling": blas_ceiling(torch, dev), "copy_ceiling": copy_ceiling(torch, dev)}),
+              flush=True)
         return
 
     wid = NAMES[args.workload]
@@ -437,7 +461,7 @@ def main():
                   f"of {osum['peak_tflops']})", file=sys.stderr, flush=True)
             others.append({"workload": name, "dtype": cname, "steps": steps, "warmup": warmup, **osum})
 
-    ceiling = blas_ceiling(torch, dev) if args.blas_ceiling else None
+    ceiling = {"gemm": blas_ceiling(torch, dev), "copy": copy_ceiling(torch, dev)} if args.blas_ceiling else None
 
     cpu = None
     if not args.no_cpu_baseline:
