@@ -25,9 +25,11 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 KINDS = [
-    (re.compile(r"k_ns_(gemm|small).*Li0E"), "ns_syrk"),
-    (re.compile(r"k_ns_(gemm|small).*Li1E"), "ns_poly"),
-    (re.compile(r"k_ns_(gemm|small).*Li[234]E"), "ns_apply"),
+    # rocprofv3 prints some names mangled (bf16 arguments) and some demangled
+    (re.compile(r"k_ns_(gemm|small)(I.*Li0E|<[^,]+, 0,)"), "ns_syrk"),
+    (re.compile(r"k_ns_(gemm|small)(I.*Li1E|<[^,]+, 1,)"), "ns_poly"),
+    (re.compile(r"k_ns_(gemm|small)(I.*Li[234]E|<[^,]+, [234],)"), "ns_apply"),
+    (re.compile(r"k_store_descs"), "store_descs"),
     (re.compile(r"k_momentum_sumsq"), "momentum_sumsq"),
     (re.compile(r"k_momentum_prep"), "momentum_prep"),
     (re.compile(r"k_prep_redo"), "prep_operand"),
