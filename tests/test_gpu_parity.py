@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from matrix_optimizers_sharded_amd.workloads import (
-    MUON_ABC, TEXTBOOK_QUINTIC_ABC, BETA, EPS, WORKLOADS, host_matrix)
+    MUON_ABC, TEXTBOOK_QUINTIC_ABC, TEXTBOOK_CUBIC_ABC, BETA, EPS, WORKLOADS, host_matrix)
 from gpu_util import (say, to_dev_f32, to_dev_bf16, host_f32, rel_err, gaussian, bf16_round,
                       run_muon, run_ns)
 
@@ -215,6 +215,19 @@ def test_textbook_quintic_bf16(gpu):
                       TEXTBOOK_QUINTIC_ABC, 5, EPS)
     worst = check_muon(grads, moms, gm, gu, "bf16", TEXTBOOK_QUINTIC_ABC, 5, label="textbook quintic bf16")
     assert worst < 5e-3
+
+
+@pytest.mark.parametrize("compute", ["f32", "bf16"])
+def test_textbook_cubic(gpu, compute):
+    """c = 0 (B' = aI + bA, the cubic iteration): both product paths, several
+    256-tiles per matrix."""
+    import torch
+    shapes = [(512, 768), (768, 512), (200, 300)]
+    grads = [gaussian(s, 430 + i, 0.02) for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 530 + i, 0.02) for i, s in enumerate(shapes)]
+    dt = torch.float32 if compute == "f32" else torch.bfloat16
+    gm, gu = run_muon(gpu, grads, moms, torch.float32, dt, torch.float32, BETA, TEXTBOOK_CUBIC_ABC, 5, EPS)
+    check_muon(grads, moms, gm, gu, compute, TEXTBOOK_CUBIC_ABC, 5, label=f"textbook cubic {compute}")
 
 
 def test_zero_matrix_gives_zero(gpu):
