@@ -46,8 +46,9 @@ constexpr int GT = GEMM_TILE;          // 256
 // workspace layout (128: 64 bf16 / 32 fp32 of k), and NSTAGE = 2 slabs are in flight
 // in an LDS ring (2 x 64 KiB, with the 32 KiB epilogue staging the whole 160 KiB),
 // so the loads of slab t+1 overlap the MFMAs of slab t.  (A four-stage ring of
-// 64-byte slabs, three slabs of load cover instead of one, measured no faster: the
-// extra barriers ate the gain.)
+// 64-byte slabs, three slabs of load cover instead of one, with this kernel: 8%
+// slower at the 7B-class owner set, SYRK 15%; 3-4% faster at the 1B- and
+// 125M-class sets, APPLY 9% there.)
 // The epilogue's stores into the workspace are non-temporal: they are read again
 // only by the next launch, so they need not displace the operand panels that the
 // other blocks of an XCD are sharing in L2.  Measured: -0.5% time for the staged
