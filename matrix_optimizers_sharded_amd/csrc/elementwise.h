@@ -43,6 +43,18 @@ template <> __device__ inline f32x4_t load4_f32<bf16_t>(const bf16_t* p) {
                  static_cast<float>(v[2]), static_cast<float>(v[3])};
 }
 
+// Non-temporal forms of load4_f32 (whole-line reads of data used once).
+template <typename T> __device__ inline f32x4_t load4_f32_nt(const T* p);
+template <> __device__ inline f32x4_t load4_f32_nt<float>(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+}
+template <> __device__ inline f32x4_t load4_f32_nt<bf16_t>(const bf16_t* p) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return f32x4_t{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                 __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
 // Pass 1, one 4096-element chunk per block.  With MOMENTUM: M <- fma(beta, M, G)
 // in place, and the chunk's sum of M^2 goes to partial[item].  Without: the sum of
 // squares of the input only.  The squares are summed in fp64: exact products, and
@@ -133,12 +145,14 @@ __global__ __launch_bounds__(256) void k_norm_scale(const MatDesc* __restrict__ 
 // and b is a multiple of 8).
 template <typename T>
 __device__ inline void store8(gptr<T> p, const float (&v)[8]);
+// The bf16 form stores non-temporally: X is written once per pass and the NS
+// products read it back from HBM (an owner set's operands exceed the caches).
 template <>
 __device__ inline void store8<bf16_t>(gptr<bf16_t> p, const float (&v)[8]) {
   bf16x8_t x;
 #pragma unroll
   for (int k = 0; k < 8; ++k) x[k] = static_cast<bf16_t>(v[k]);
-  *reinterpret_cast<gptr<bf16x8_t>>(p) = x;
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), reinterpret_cast<gptr<u32x4_t>>(p));
 }
 template <>
 __device__ inline void store8<float>(gptr<float> p, const float (&v)[8]) {
@@ -180,7 +194,11 @@ __device__ inline void write_operand_tile(const MatDesc& d, int i0, int j0,
 // and B'(sX) = s B'X.
 // Four tiles per block (2 blocks per CU by LDS) measured fastest: 5.1-5.7 TB/s
 // against 4.7-5.3 TB/s with one tile per block at the 7B-class owner set, as more
-// of each thread's loads are in flight before its first store.
+// of each thread's loads are in flight before its first store.  Every access of the
+// whole-tile path covers whole 128-byte lines per instruction, and all of them are
+// non-temporal (G, M read once; M, X written once and not read again in this pass):
+// 12.3-13.2 ms per pass at the 7B-class set against 14.0-15.2 ms with ordinary
+// accesses (two boxes, three rounds each); non-temporal loads alone gave 12.8-14.9.
 constexpr int MP_TPB = 4;
 template <typename TG, typename TC, bool MOMENTUM>
 __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict__ descs, int count,
@@ -230,8 +248,8 @@ __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict
       for (int q = 0; q < 4; ++q) {
         const int a = (t >> 4) + 16 * q, b = (t & 15) * 4;
         const int64_t e = (src_r0(u) + a) * ld + src_c0(u) + b;
-        gv[u][q] = load4_f32<TG>(g + e);
-        if (MOMENTUM) mv[u][q] = *reinterpret_cast<const f32x4_t*>(m + e);
+        gv[u][q] = load4_f32_nt<TG>(g + e);
+        if (MOMENTUM) mv[u][q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(m + e));
       }
 #pragma unroll
     for (int u = 0; u < MP_TPB; ++u)
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(256) void k_momentum_prep(const MatDesc* __restrict
         if (MOMENTUM) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(beta, mv[u][q][k], gv[u][q][k]);
-          *reinterpret_cast<f32x4_t*>(m + (src_r0(u) + a) * ld + src_c0(u) + b) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(m + (src_r0(u) + a) * ld + src_c0(u) + b));
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -345,111 +363,133 @@ __global__ __launch_bounds__(256) void k_scaled_copy(const MatDesc* __restrict__
 // ---------------------------------------------------------------------------
 // Sign-Muon tail.
 
-// The sign kernels work in units of 256 threads x 8 elements (one packed byte per
-// thread); a block covers *_UNITS consecutive units, and each thread issues the
-// loads of all its units before it stores anything.  Measured at 2^28 elements
-// (fp32 pack input, bf16 unpack output), one box, three rounds each:
-//   sign_pack    1 unit 4.73 TB/s; 2 units 4.50; 4 units 4.40
-//   sign_unpack  1 unit 4.65 TB/s; 2 units 5.27; 4 units 5.46
-//   sign_apply   1 unit 5.75 TB/s; 2 units 5.54; 4 units 5.33 (fp32 weight)
-constexpr int PACK_UNITS = 1;
-constexpr int UNPACK_UNITS = 4;
-constexpr int SAPPLY_UNITS = 1;
+constexpr int UNPACK_PIECES = 4;
+constexpr int SAPPLY_PIECES = 2;
 
-// The byte of the 8 consecutive elements from e0 (bit k = (u[e0 + k] >= 0)).
+// sign_pack: each lane of a wave reads PACK_LOADS 16-byte pieces (4 fp32 or 8 bf16
+// elements each), the 64 lanes of one load on 64 consecutive pieces, so that every
+// load instruction reads 1 KiB of whole cache lines.  The loads are non-temporal:
+// with ordinary loads the pack ran at 6.3 TB/s on its own but 4.7 TB/s right after a
+// kernel that had written 1 GiB (the tail of an optimizer step), against 6.4 and
+// 6.1 TB/s non-temporal (2^28 fp32 elements).  Non-temporal loads of pieces that do
+// not cover whole lines per instruction were slower than ordinary ones.
+constexpr int PACK_LOADS = 2;
+
+// Sign bits of the 16 / sizeof(T) elements of one 16-byte piece as loaded (bit k =
+// element k >= 0; a bf16 value widens to fp32 exactly by moving it to the high half).
 template <typename T>
-__device__ inline uint32_t sign_byte(const T* __restrict__ u, int64_t e0, int64_t numel, int vec_ok) {
-  uint32_t byte = 0;
-  if (vec_ok && e0 + 8 <= numel) {
-    if (sizeof(T) == 4) {
-      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(u + e0);
-      const f32x4_t x0 = p[0], x1 = p[1];
+__device__ inline uint32_t piece_bits(const u32x4_t v) {
+  uint32_t bits = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        byte |= static_cast<uint32_t>(x0[k] >= 0.f) << k;
-        byte |= static_cast<uint32_t>(x1[k] >= 0.f) << (k + 4);
-      }
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (sizeof(T) == 4) {
+      bits |= static_cast<uint32_t>(__uint_as_float(v[q]) >= 0.f) << q;
     } else {
-      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(u + e0);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) byte |= static_cast<uint32_t>(static_cast<float>(x[k]) >= 0.f) << k;
-    }
-  } else {
-    for (int k = 0; k < 8; ++k) {
-      const int64_t e = e0 + k;
-      if (e < numel) byte |= static_cast<uint32_t>(static_cast<float>(u[e]) >= 0.f) << k;
+      bits |= static_cast<uint32_t>(__uint_as_float(v[q] << 16) >= 0.f) << (2 * q);
+      bits |= static_cast<uint32_t>(__uint_as_float(v[q] & 0xFFFF0000u) >= 0.f) << (2 * q + 1);
     }
   }
-  return byte;
+  return bits;
 }
 
-// One thread per 8 consecutive elements of each unit -> one byte; 4 lanes OR their
-// bytes into a 32-bit word (element i -> bit i % 32 of word i / 32).  bit = (u >= 0).
-// Row y of the grid packs worker y: its numel values start at u + y * u_stride and
-// its words at packed + y * nwords (the [M][nwords] stack a vote reads), so M
-// workers take one launch.  (A grid of a few blocks per CU looping over the bytes,
-// four per thread per round, was slower at 2^28 elements: 3.98 against 4.71 TB/s.)
+// Element i -> bit i % 32 of word i / 32, bit = (u >= 0): the G = 32 / EPL lanes
+// whose pieces make up one word OR their bits together.  Row y of the grid packs
+// worker y: its numel values start at u + y * u_stride and its words at packed + y *
+// nwords (the [M][nwords] stack a vote reads), so M workers take one launch.  A
+// piece that runs past numel, or any piece when the rows are not 16-byte aligned,
+// is read element by element; bits past numel stay 0.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sign_pack(const T* __restrict__ u, int64_t u_stride, int64_t numel,
                                                    uint32_t* __restrict__ packed, int vec_ok) {
+  constexpr int EPL = 16 / static_cast<int>(sizeof(T));   // elements per piece
+  constexpr int G = 32 / EPL;                              // lanes per word
   const int lane = threadIdx.x & 63;
   const int64_t nwords = (numel + 31) >> 5;
   u += static_cast<int64_t>(blockIdx.y) * u_stride;
   packed += static_cast<int64_t>(blockIdx.y) * nwords;
-  uint32_t bytes[PACK_UNITS];
+  const int64_t load0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * PACK_LOADS;
+  u32x4_t v[PACK_LOADS];
+  bool full[PACK_LOADS];
 #pragma unroll
-  for (int s = 0; s < PACK_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * PACK_UNITS + s) * 256 + threadIdx.x;
-    bytes[s] = sign_byte(u, t * 8, numel, vec_ok);
+  for (int h = 0; h < PACK_LOADS; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
+    full[h] = vec_ok && e0 + EPL <= numel;
+    if (full[h]) v[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(u + e0));
   }
 #pragma unroll
-  for (int s = 0; s < PACK_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * PACK_UNITS + s) * 256 + threadIdx.x;
-    uint32_t w = bytes[s] << (8 * (lane & 3));
-    w |= __shfl_xor(w, 1, 64);
-    w |= __shfl_xor(w, 2, 64);
-    if ((lane & 3) == 0 && (t >> 2) < nwords) packed[t >> 2] = w;
+  for (int h = 0; h < PACK_LOADS; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
+    uint32_t bits = 0;
+    if (full[h]) {
+      bits = piece_bits<T>(v[h]);
+    } else {
+      for (int k = 0; k < EPL; ++k)
+        if (e0 + k < numel) bits |= static_cast<uint32_t>(static_cast<float>(u[e0 + k]) >= 0.f) << k;
+    }
+    uint32_t w = bits << (EPL * (lane % G));
+#pragma unroll
+    for (int x = 1; x < G; x <<= 1) w |= __shfl_xor(w, x, 64);
+    const int64_t word = e0 >> 5;
+    if (lane % G == 0 && word < nwords) packed[word] = w;
   }
 }
 
 __device__ inline uint32_t lane_word(uint32_t v, int) { return v; }
 __device__ inline uint32_t lane_word(const u32x4_t& v, int q) { return v[q]; }
 
+// Loads of the vote: the four-word path reads 1 KiB of whole lines per instruction
+// and loads non-temporally (as sign_pack does); the one-word path reads 256 bytes
+// per instruction and loads normally.
+__device__ inline uint32_t vote_load(const uint32_t* p) { return *p; }
+__device__ inline u32x4_t vote_load(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
+
 // Vote of one group of W (1 or 4) consecutive words: a bit-sliced counter of LV bit
 // planes (2^LV > M) adds the M workers' words (all 32 bit positions of every word at
 // once), and a bit-sliced compare gives count >= ceil(M/2), which is
 // 2*count - M >= 0 (ties -> +1).  Loads are issued 8 workers at a time ahead of the
 // additions.  V is uint32_t or a 4-vector of them.
-template <typename V, int LV>
-__device__ inline V vote_group(const V* __restrict__ src, int64_t stride, int M, V (&cnt)[LV]) {
+template <typename V, int LV, int NG>
+__device__ inline void vote_groups(const V* __restrict__ src, int64_t gstep, int64_t stride, int M,
+                                   V (&cnt)[NG][LV], V (&res)[NG]) {
 #pragma unroll
-  for (int l = 0; l < LV; ++l) cnt[l] = V{} ^ V{};
-  auto add = [&](V carry) {
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int l = 0; l < LV; ++l) cnt[g][l] = V{} ^ V{};
+  auto add = [&](V (&c)[LV], V carry) {
 #pragma unroll
     for (int l = 0; l < LV; ++l) {
-      const V c = cnt[l];
-      cnt[l] = c ^ carry;
-      carry = c & carry;
+      const V o = c[l];
+      c[l] = o ^ carry;
+      carry = o & carry;
     }
   };
   int k = 0;
   for (; k + 8 <= M; k += 8) {
-    V x[8];
+    V x[8][NG];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = src[static_cast<int64_t>(k + u) * stride];
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(x[u]);
+      for (int g = 0; g < NG; ++g) x[u][g] = vote_load(src + g * gstep + static_cast<int64_t>(k + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) add(cnt[g], x[u][g]);
   }
-  for (; k < M; ++k) add(src[static_cast<int64_t>(k) * stride]);
+  for (; k < M; ++k)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) add(cnt[g], vote_load(src + g * gstep + static_cast<int64_t>(k) * stride));
   // count >= T with T = ceil(M/2) <=> carry out of count + (2^LV - T)
   const uint32_t addend = (1u << LV) - static_cast<uint32_t>((M + 1) >> 1);
-  V carry = V{} ^ V{};
 #pragma unroll
-  for (int l = 0; l < LV; ++l) {
-    const V kbits = V{} ^ V{} ^ (((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u);
-    carry = (cnt[l] & kbits) | ((cnt[l] ^ kbits) & carry);
+  for (int g = 0; g < NG; ++g) {
+    V carry = V{} ^ V{};
+#pragma unroll
+    for (int l = 0; l < LV; ++l) {
+      const V kbits = V{} ^ V{} ^ (((addend >> l) & 1u) ? 0xFFFFFFFFu : 0u);
+      carry = (cnt[g][l] & kbits) | ((cnt[g][l] ^ kbits) & carry);
+    }
+    res[g] = carry;
   }
-  return carry;
 }
 
 // int8 sums 2*count - M of the n (<= 32) elements of one word, word q of the group,
@@ -467,9 +507,14 @@ __device__ inline void vote_sums(const V (&cnt)[LV], int q, int M, int n, int8_t
   }
 }
 
-// One thread per 4 packed words (16-byte loads) when the buffers allow it, else one
-// per word.  Pad bits of the last word are cleared.  LV bit planes count up to
-// 2^LV - 1 workers; SUMS also writes the int8 sums.
+// quad = 0: a thread votes one word.  quad = 1 (the buffers allow 16-byte loads): a
+// thread votes one group of 4 words, a block 256 groups.  quad = 2: two groups 256
+// apart, a block 512 groups, with twice the loads in flight per thread; 4% more
+// bandwidth at 2^28 elements (5.8 against 5.6 TB/s), but 1 us slower at 2^24, where
+// the vote is latency-bound and wants more blocks.  Pad bits of the last word are
+// cleared.  LV bit planes count up to 2^LV - 1 workers; SUMS also writes the int8
+// sums.
+constexpr int64_t VOTE_PAIR_GROUPS = int64_t(1) << 20;
 template <int LV, bool SUMS>
 __global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ packed, int M, int64_t numel,
                                                    int64_t nwords, uint32_t* __restrict__ out,
@@ -480,106 +525,131 @@ __global__ __launch_bounds__(256) void k_sign_vote(const uint32_t* __restrict__ 
     out[w] = tail < 32 ? word & ((1u << tail) - 1u) : word;
   };
   if (quad) {
-    // nwords % 4 == 0: every thread below nwords / 4 owns four whole words
-    const int64_t w0 = t * 4;
-    if (w0 >= nwords) return;
-    u32x4_t cnt[LV];
-    const u32x4_t v = vote_group<u32x4_t, LV>(reinterpret_cast<const u32x4_t*>(packed + w0), nwords / 4, M, cnt);
+    // nwords % 4 == 0: groups (four whole words) b * per + tid and, for quad = 2,
+    // b * per + 256 + tid of block b, both in one pass where both exist
+    const int64_t nq = nwords / 4;
+    const int64_t qa = static_cast<int64_t>(blockIdx.x) * (quad == 2 ? 512 : 256) + threadIdx.x;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(packed);
+    auto emit = [&](int64_t q4, const u32x4_t& v, const u32x4_t (&cnt)[LV]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      finish(w0 + q, v[q]);
-      if (SUMS) {
-        const int64_t tail = numel - (w0 + q) * 32;
-        vote_sums<u32x4_t, LV>(cnt, q, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + (w0 + q) * 32);
+      for (int q = 0; q < 4; ++q) {
+        finish(q4 * 4 + q, v[q]);
+        if (SUMS) {
+          const int64_t tail = numel - (q4 * 4 + q) * 32;
+          vote_sums<u32x4_t, LV>(cnt, q, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + (q4 * 4 + q) * 32);
+        }
       }
+    };
+    if (quad == 2 && qa + 256 < nq) {
+      u32x4_t cnt[2][LV], v[2];
+      vote_groups<u32x4_t, LV, 2>(src + qa, 256, nq, M, cnt, v);
+      emit(qa, v[0], cnt[0]);
+      emit(qa + 256, v[1], cnt[1]);
+    } else if (qa < nq) {
+      u32x4_t cnt[1][LV], v[1];
+      vote_groups<u32x4_t, LV, 1>(src + qa, 0, nq, M, cnt, v);
+      emit(qa, v[0], cnt[0]);
     }
   } else {
     if (t >= nwords) return;
-    uint32_t cnt[LV];
-    finish(t, vote_group<uint32_t, LV>(packed + t, nwords, M, cnt));
+    uint32_t cnt[1][LV], v[1];
+    vote_groups<uint32_t, LV, 1>(packed + t, 0, nwords, M, cnt, v);
+    finish(t, v[0]);
     if (SUMS) {
       const int64_t tail = numel - t * 32;
-      vote_sums<uint32_t, LV>(cnt, 0, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + t * 32);
+      vote_sums<uint32_t, LV>(cnt[0], 0, M, tail < 32 ? static_cast<int>(tail) : 32, out_sum + t * 32);
     }
   }
 }
 
+// sign_unpack and sign_apply: each lane handles *_PIECES 16-byte pieces of the
+// output (4 fp32 or 8 bf16 elements each), the 64 lanes of one access on 64
+// consecutive pieces, so that each load and store instruction covers 1 KiB of whole
+// lines; the lanes of one word read it together.  Output stores, and sign_apply's
+// loads of the weight, are non-temporal.
+template <typename T> __device__ inline uint32_t bits_of(T v) {
+  if constexpr (sizeof(T) == 4) return __float_as_uint(v);
+  else return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, v));
+}
+template <typename T> __device__ inline T of_bits(uint32_t b) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float(b);
+  else return __builtin_bit_cast(bf16_t, static_cast<uint16_t>(b));
+}
+// element k of a 16-byte piece as fp32, and the piece with element k replaced
+template <typename T> __device__ inline float piece_get(const u32x4_t& v, int k) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float(v[k]);
+  else return __uint_as_float((k & 1) ? (v[k >> 1] & 0xFFFF0000u) : (v[k >> 1] << 16));
+}
+template <typename T> __device__ inline void piece_set(u32x4_t& v, int k, float x) {
+  if constexpr (sizeof(T) == 4) {
+    v[k] = __float_as_uint(x);
+  } else {
+    const uint32_t h = bits_of(static_cast<bf16_t>(x));
+    v[k >> 1] = (k & 1) ? ((v[k >> 1] & 0xFFFFu) | (h << 16)) : ((v[k >> 1] & 0xFFFF0000u) | h);
+  }
+}
+
 // The inverse of the packing, for the local polar step on the voted signs: element
-// i <- +1 where bit i is set, else -1.  One thread per 8 elements (one byte).
+// i <- +1 where bit i is set, else -1.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sign_unpack(const uint32_t* __restrict__ packed, int64_t numel,
                                                      T* __restrict__ out, int vec_ok) {
-  uint32_t words[UNPACK_UNITS];
+  constexpr int EPL = 16 / static_cast<int>(sizeof(T));
+  const int lane = threadIdx.x & 63;
+  const int64_t load0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * UNPACK_PIECES;
+  uint32_t words[UNPACK_PIECES];
 #pragma unroll
-  for (int s = 0; s < UNPACK_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * UNPACK_UNITS + s) * 256 + threadIdx.x;
-    words[s] = t * 8 < numel ? packed[t >> 2] : 0u;
+  for (int h = 0; h < UNPACK_PIECES; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
+    words[h] = e0 < numel ? packed[e0 >> 5] : 0u;
   }
 #pragma unroll
-  for (int s = 0; s < UNPACK_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * UNPACK_UNITS + s) * 256 + threadIdx.x;
-    const int64_t e0 = t * 8;
+  for (int h = 0; h < UNPACK_PIECES; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
     if (e0 >= numel) continue;
-    const uint32_t byte = (words[s] >> (8 * (t & 3))) & 0xFFu;
-    float v[8];
+    const uint32_t bits = words[h] >> (e0 & 31);
+    if (vec_ok && e0 + EPL <= numel) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = ((byte >> k) & 1u) ? 1.f : -1.f;
-    if (vec_ok && e0 + 8 <= numel) {
-      if (sizeof(T) == 4) {
-        f32x4_t* p = reinterpret_cast<f32x4_t*>(out + e0);
-        p[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-        p[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-      } else {
-        bf16x8_t x;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = static_cast<bf16_t>(v[k]);
-        *reinterpret_cast<bf16x8_t*>(out + e0) = x;
-      }
+      for (int k = 0; k < EPL; ++k) piece_set<T>(v, k, ((bits >> k) & 1u) ? 1.f : -1.f);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + e0));
     } else {
-      for (int k = 0; k < 8 && e0 + k < numel; ++k) out[e0 + k] = from_f32<T>(v[k]);
+      for (int k = 0; k < EPL && e0 + k < numel; ++k) out[e0 + k] = from_f32<T>(((bits >> k) & 1u) ? 1.f : -1.f);
     }
   }
 }
 
 // Sign-Muon parameter update W <- W - lr * S with S = +1 where bit i is set, else
-// -1: the difference is formed in fp32 and stored in W's dtype.  One thread per 8
-// elements of each unit.
+// -1: the difference is formed in fp32 and stored in W's dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sign_apply(const uint32_t* __restrict__ packed, int64_t numel,
                                                     T* __restrict__ w, float lr, int vec_ok) {
-  typedef typename std::conditional<sizeof(T) == 4, f32x4_t, bf16x8_t>::type v_t;   // 16 bytes
-  constexpr int NV = sizeof(T) == 4 ? 2 : 1;                                        // per 8 elements
-  uint32_t words[SAPPLY_UNITS];
-  v_t x[SAPPLY_UNITS][NV];
+  constexpr int EPL = 16 / static_cast<int>(sizeof(T));
+  const int lane = threadIdx.x & 63;
+  const int64_t load0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * SAPPLY_PIECES;
+  uint32_t words[SAPPLY_PIECES];
+  u32x4_t x[SAPPLY_PIECES];
+  bool full[SAPPLY_PIECES];
 #pragma unroll
-  for (int s = 0; s < SAPPLY_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * SAPPLY_UNITS + s) * 256 + threadIdx.x;
-    const int64_t e0 = t * 8;
-    words[s] = e0 < numel ? packed[t >> 2] : 0u;
-    if (vec_ok && e0 + 8 <= numel) {
-#pragma unroll
-      for (int h = 0; h < NV; ++h) x[s][h] = reinterpret_cast<const v_t*>(w + e0)[h];
-    }
+  for (int h = 0; h < SAPPLY_PIECES; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
+    words[h] = e0 < numel ? packed[e0 >> 5] : 0u;
+    full[h] = vec_ok && e0 + EPL <= numel;
+    if (full[h]) x[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(w + e0));
   }
 #pragma unroll
-  for (int s = 0; s < SAPPLY_UNITS; ++s) {
-    const int64_t t = (static_cast<int64_t>(blockIdx.x) * SAPPLY_UNITS + s) * 256 + threadIdx.x;
-    const int64_t e0 = t * 8;
+  for (int h = 0; h < SAPPLY_PIECES; ++h) {
+    const int64_t e0 = ((load0 + h) * 64 + lane) * EPL;
     if (e0 >= numel) continue;
-    const uint32_t byte = (words[s] >> (8 * (t & 3))) & 0xFFu;
-    if (vec_ok && e0 + 8 <= numel) {
+    const uint32_t bits = words[h] >> (e0 & 31);
+    if (full[h]) {
+      u32x4_t y = x[h];
 #pragma unroll
-      for (int h = 0; h < NV; ++h) {
-        v_t y = x[s][h];
-        constexpr int PER = 8 / NV;
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-          y[k] = from_f32<T>(to_f32(y[k]) - (((byte >> (h * PER + k)) & 1u) ? lr : -lr));
-        reinterpret_cast<v_t*>(w + e0)[h] = y;
-      }
+      for (int k = 0; k < EPL; ++k) piece_set<T>(y, k, piece_get<T>(x[h], k) - (((bits >> k) & 1u) ? lr : -lr));
+      __builtin_nontemporal_store(y, reinterpret_cast<u32x4_t*>(w + e0));
     } else {
-      for (int k = 0; k < 8 && e0 + k < numel; ++k)
-        w[e0 + k] = from_f32<T>(to_f32(w[e0 + k]) - (((byte >> k) & 1u) ? lr : -lr));
+      for (int k = 0; k < EPL && e0 + k < numel; ++k)
+        w[e0 + k] = from_f32<T>(to_f32(w[e0 + k]) - (((bits >> k) & 1u) ? lr : -lr));
     }
   }
 }

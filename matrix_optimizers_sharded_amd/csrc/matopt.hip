@@ -546,8 +546,9 @@ int32_t sign_pack_batched(const void* u, int32_t dtype, int32_t M, int64_t numel
   if (M < 1 || M > 65535) return fail(MO_ERR_INVALID, "M must be in [1, 65535]");
   if (M > 1 && u_stride < numel) return fail(MO_ERR_INVALID, "u_stride must be >= numel when M > 1");
   if (!u || !packed) return fail(MO_ERR_INVALID, "u or packed is NULL");
-  const int64_t threads = ((numel + 31) / 32) * 4;
-  const int64_t blocks = (threads + 256 * PACK_UNITS - 1) / (256 * PACK_UNITS);
+  // a block covers 4 waves x PACK_LOADS loads x 64 lanes x 16 bytes
+  const int64_t per_block = 256 * PACK_LOADS * (16 / dtype_size(dtype));
+  const int64_t blocks = (numel + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   // 16-byte loads when every worker's values start 16-byte aligned
@@ -575,11 +576,13 @@ int32_t sign_vote(const uint32_t* packed, int32_t M, int64_t numel, uint32_t* ou
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !out_packed) return fail(MO_ERR_INVALID, "packed or out_packed is NULL");
   const int64_t nwords = (numel + 31) / 32;
-  // four words per thread with 16-byte loads when every worker's row starts 16-byte
-  // aligned (nwords % 4 == 0 and an aligned base)
-  const int quad = (nwords % 4 == 0 && aligned16(packed)) ? 1 : 0;
-  const int64_t threads = quad ? nwords / 4 : nwords;
-  const int64_t blocks = (threads + 255) / 256;
+  // groups of four words with 16-byte loads when every worker's row starts 16-byte
+  // aligned (nwords % 4 == 0 and an aligned base); two groups per thread when that
+  // still leaves at least 8 blocks of 512 groups per CU (2^20 groups)
+  int quad = (nwords % 4 == 0 && aligned16(packed)) ? 1 : 0;
+  if (quad && nwords / 4 >= VOTE_PAIR_GROUPS) quad = 2;
+  const int64_t per_block = quad == 2 ? 512 : 256;   // groups or words
+  const int64_t blocks = ((quad ? nwords / 4 : nwords) + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   // the counter needs 2^LV > M: 4 bit planes up to 15 workers, 8 up to 255, else 16
@@ -605,7 +608,8 @@ int32_t sign_unpack(const uint32_t* packed, int64_t numel, int32_t dtype, void* 
   if (!valid_dtype(dtype)) return fail(MO_ERR_UNSUPPORTED, "dtype must be MO_F32 or MO_BF16");
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !out) return fail(MO_ERR_INVALID, "packed or out is NULL");
-  const int64_t blocks = ((numel + 7) / 8 + 256 * UNPACK_UNITS - 1) / (256 * UNPACK_UNITS);
+  const int64_t per_block = 256 * UNPACK_PIECES * (16 / dtype_size(dtype));
+  const int64_t blocks = (numel + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int vec = aligned16(out) ? 1 : 0;
@@ -626,7 +630,8 @@ int32_t sign_apply(const uint32_t* packed, int64_t numel, int32_t dtype, void* w
   if (numel < 1) return fail(MO_ERR_INVALID, "numel must be >= 1");
   if (!packed || !weight) return fail(MO_ERR_INVALID, "packed or weight is NULL");
   if (!std::isfinite(lr)) return fail(MO_ERR_INVALID, "lr must be finite");
-  const int64_t blocks = ((numel + 7) / 8 + 256 * SAPPLY_UNITS - 1) / (256 * SAPPLY_UNITS);
+  const int64_t per_block = 256 * SAPPLY_PIECES * (16 / dtype_size(dtype));
+  const int64_t blocks = (numel + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return fail(MO_ERR_INVALID, "numel too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int vec = aligned16(weight) ? 1 : 0;

@@ -49,13 +49,14 @@ def test_sign_unpack_bit_exact(gpu, dtype, numel):
     np.testing.assert_array_equal(host_f32(out), oracle.unpack_signs(words, numel))
 
 
-def test_sign_unpack_unaligned_output(gpu):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sign_unpack_unaligned_output(gpu, dtype):
     import torch
     from matrix_optimizers_sharded_amd import sign_unpack
     numel = 1000
     words = random_words(numel, 5)
-    buf = torch.zeros(numel + 1, dtype=torch.float32, device=gpu)
-    sign_unpack(dev_words(words, gpu), numel, out=buf[1:])          # 4-byte offset: scalar path
+    buf = torch.zeros(numel + 1, dtype=tdt(dtype), device=gpu)
+    sign_unpack(dev_words(words, gpu), numel, out=buf[1:])          # one element off: scalar path
     torch.cuda.synchronize()
     got = host_f32(buf)
     assert got[0] == 0.0
@@ -82,6 +83,28 @@ def test_sign_apply_bit_exact(gpu, dtype, numel, lr):
     torch.cuda.synchronize()
     want = oracle.sign_update(w0, words, lr, bf16=(dtype == "bf16"))
     np.testing.assert_array_equal(host_f32(w).astype(np.float64), want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sign_apply_unaligned_weight(gpu, dtype):
+    """A weight view one element past a 16-byte boundary takes the element-by-element
+    path; the element before the view is left alone."""
+    import torch
+    from matrix_optimizers_sharded_amd import sign_apply
+    numel = 5000
+    say(f"sign_apply unaligned dtype={dtype} numel={numel}")
+    words = random_words(numel, 11)
+    w0 = gaussian(numel + 1, 12, 0.02)
+    if dtype == "bf16":
+        bits, w0 = bf16_round(w0)
+        buf = to_dev_bf16(bits, gpu)
+    else:
+        buf = to_dev_f32(w0, gpu)
+    sign_apply(dev_words(words, gpu), buf[1:], 1e-3)
+    torch.cuda.synchronize()
+    got = host_f32(buf).astype(np.float64)
+    assert got[0] == w0[0]
+    np.testing.assert_array_equal(got[1:], oracle.sign_update(w0[1:], words, 1e-3, bf16=(dtype == "bf16")))
 
 
 def test_vote_then_apply_and_polar_step(gpu):

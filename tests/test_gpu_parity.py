@@ -87,7 +87,9 @@ def test_sign_pack_batched_bit_exact(gpu, dtype, M, numel, pad):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 15, 16, 127])
-@pytest.mark.parametrize("numel", [1, 33, 1000, 65537])
+# 169465 elements: 5296 words, a multiple of 4: the four-word path over several
+# blocks, the last one ragged
+@pytest.mark.parametrize("numel", [1, 33, 1000, 65537, 169465])
 def test_sign_vote_bit_exact(gpu, M, numel):
     import torch
     from matrix_optimizers_sharded_amd import sign_vote
@@ -115,14 +117,15 @@ def test_sign_vote_large_M_without_sums(gpu):
 
 
 @pytest.mark.parametrize("M", [5, 15, 16, 255, 256, 1000])
-def test_sign_vote_four_word_path(gpu, M):
-    """nwords a multiple of 4 on a 16-byte aligned buffer takes the 4-words-per-thread
-    path; the same words on a base shifted by one word take the one-word path.  The M
-    values straddle the counter depths (4 bit planes up to 15 workers, 8 up to 255)."""
+@pytest.mark.parametrize("nwords", [1024, 3248])
+def test_sign_vote_four_word_path(gpu, M, nwords):
+    """nwords a multiple of 4 on a 16-byte aligned buffer takes the four-word path
+    (1024 words: one block; 3248: four blocks, the last ragged); the same words on a
+    base shifted by one word take the one-word path.  The M values straddle the
+    counter depths (4 bit planes up to 15 workers, 8 up to 255)."""
     import torch
     from matrix_optimizers_sharded_amd import sign_vote
-    numel = 1024 * 32 - 3
-    nwords = 1024
+    numel = nwords * 32 - 3
     rng = np.random.default_rng(M)
     packed = rng.integers(0, 2 ** 32, size=(M, nwords), dtype=np.uint64).astype(np.uint32)
     packed[:, -1] &= np.uint32((1 << (numel % 32)) - 1)
@@ -136,6 +139,25 @@ def test_sign_vote_four_word_path(gpu, M):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want)
     np.testing.assert_array_equal(out2.cpu().numpy().view(np.uint32), want)
+
+
+def test_sign_vote_two_groups_per_thread(gpu):
+    """From 2^20 groups of four words on, a thread votes two groups 256 apart: here
+    2^20 + 300 groups, so the last block has threads with two groups and threads with
+    one.  With the int8 sums."""
+    import torch
+    from matrix_optimizers_sharded_amd import sign_vote
+    M, nwords = 3, 4 * ((1 << 20) + 300)
+    numel = nwords * 32 - 3
+    say(f"sign_vote two groups per thread M={M} nwords={nwords}")
+    rng = np.random.default_rng(77)
+    packed = rng.integers(0, 2 ** 32, size=(M, nwords), dtype=np.uint64).astype(np.uint32)
+    packed[:, -1] &= np.uint32((1 << (numel % 32)) - 1)
+    out, sums = sign_vote(torch.from_numpy(packed.view(np.int32)).to(gpu), numel, with_sums=True)
+    torch.cuda.synchronize()
+    want_out, want_sums = oracle.majority_vote(packed, numel)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want_out)
+    np.testing.assert_array_equal(sums.cpu().numpy(), want_sums.astype(np.int8))
 
 
 # ---------------------------------------------------------------- Muon step
