@@ -42,6 +42,16 @@
  *     a message (thread-local).  Faults inside kernels surface at the caller's
  *     next synchronisation.
  *   - Calls that share a workspace must be ordered on one stream.
+ *   - muon_step_batched, muon_step_apply and ns_orthogonalize may run half of
+ *     their Newton-Schulz products on a second stream of the library's own (one
+ *     per device, created on first use with the default priority and kept for the
+ *     life of the process): they do so when a product's launch holds fewer than
+ *     16 rounds of 256x256 tiles per CU, not while `stream` is being captured
+ *     into a graph, and never in muon_step_batched_noalloc.  That stream waits
+ *     for everything enqueued on `stream` before the call, and `stream` waits for
+ *     it before anything enqueued after the call, so the ordering seen from
+ *     `stream` is the same as with one stream.  Results do not depend on it: each
+ *     matrix is computed by the same kernels tile by tile either way.
  */
 #ifndef MATOPT_H
 #define MATOPT_H
@@ -53,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MATOPT_VERSION 110
+#define MATOPT_VERSION 111
 
 /* element types */
 enum { MO_F32 = 0, MO_BF16 = 1 };
@@ -226,7 +236,9 @@ const char *mo_last_error(void);
 int32_t mo_version(void);
 
 /* Per-kernel timing for measurement.  mo_profile_begin() makes the calls above
- * record a HIP event pair around every kernel they launch (on the call's stream);
+ * record a HIP event pair around every kernel they launch (on the stream it runs
+ * on: the call's, or the library's second stream for half of a split product, whose
+ * records then overlap in time with the other half's);
  * mo_profile_end() waits for those events and fills up to `max` records, one per
  * kernel kind, returning how many kinds were seen (or a negative code).
  * Profiling state is process-wide and guarded by a lock, so calls from several

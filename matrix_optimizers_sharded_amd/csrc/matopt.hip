@@ -15,7 +15,9 @@
 // Each launch covers every matrix of the batch (grouped launch); blocks find their
 // matrix by binary search over the table, which is sorted by decreasing size so
 // the longest tiles start first.  The GEMM launches are persistent: one block per
-// CU, each walking a strided share of the tile list.
+// CU, each walking a strided share of the tile list.  When those launches hold only
+// a few rounds of tiles, the batch is cut into two halves whose products run on the
+// caller's stream and on a second stream of the library's own (split_wanted).
 
 #include <hip/hip_runtime.h>
 
@@ -23,6 +25,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <mutex>
 #include <numeric>
 #include <string>
@@ -87,13 +90,20 @@ struct Plan {
   std::vector<MatDesc> descs;
   int64_t total[NKIND] = {};
   size_t off_desc = 0, off_scale = 0, off_partial = 0, bytes = 0;
+  // Split plans (see split_wanted): descriptors [0, split_at) are half A, the rest
+  // half B; the 256-tile GEMM kinds number their items from 0 in each half, and
+  // half_total[h][kind] counts them (the other kinds number across the whole table).
+  int split_at = 0;
+  int64_t half_total[2][3] = {};
 };
+// the GEMM kinds a split plan numbers per half
+bool per_half_kind(int kd) { return kd == KIND_SYRK || kd == KIND_POLY || kd == KIND_APPLY; }
 // The per-matrix scalars at off_scale: scale[count] (s = 1 / (||M||_F + eps)),
 // first[count] (the factor the first NS products apply) and redo[count] (int flags).
 
 // Validate the list and lay out the workspace.  base == nullptr only sizes it.
 int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, unsigned char* base,
-               Plan& plan, int in_dtype = MO_F32, int out_dtype = MO_F32) {
+               Plan& plan, int in_dtype = MO_F32, int out_dtype = MO_F32, bool split = false) {
   if (count < 0) return fail(MO_ERR_INVALID, "count must be >= 0");
   if (count > 0 && !mats) return fail(MO_ERR_INVALID, "mats is NULL");
   if (!valid_dtype(compute)) return fail(MO_ERR_UNSUPPORTED, "compute dtype must be MO_F32 or MO_BF16");
@@ -116,6 +126,15 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
   std::stable_sort(order.begin(), order.end(), [&](int p, int q) {
     return mats[p].rows * mats[p].cols > mats[q].rows * mats[q].cols;
   });
+  if (split && count >= 2) {
+    // half A: every other matrix of the sorted order from the first, half B the
+    // rest, so both halves hold the same mix of shapes (each still sorted)
+    std::vector<int> halves;
+    for (int h = 0; h < 2; ++h)
+      for (int k = h; k < count; k += 2) halves.push_back(order[k]);
+    order.swap(halves);
+    plan.split_at = (count + 1) / 2;
+  }
   size_t off = 0;
   plan.off_desc = off;
   off = align_up(off + sizeof(MatDesc) * std::max(count, 1), ALIGN);
@@ -182,8 +201,14 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.items[KIND_SMALL_RECT] = small ? small_rect_items(d.m, d.n) : 0;
     d.items[KIND_PREP] = (int64_t(d.mp) / PREP_TILE) * (int64_t(d.np) / PREP_TILE);
     d.items[KIND_CHUNK] = (d.numel + CHUNK - 1) / CHUNK;
+    const int h = (plan.split_at > 0 && k >= plan.split_at) ? 1 : 0;
     for (int kd = 0; kd < NKIND; ++kd) {
-      d.begin[kd] = plan.total[kd];
+      if (plan.split_at > 0 && per_half_kind(kd)) {
+        d.begin[kd] = plan.half_total[h][kd - KIND_SYRK];
+        plan.half_total[h][kd - KIND_SYRK] += d.items[kd];
+      } else {
+        d.begin[kd] = plan.total[kd];
+      }
       plan.total[kd] += d.items[kd];
     }
   }
@@ -275,64 +300,169 @@ struct ApplyOpt {
   float lr = 0.f;
 };
 
-// k NS iterations: per product one persistent 256 x 256-tile launch over the
-// matrices with m > 256 and one 32 x 32-block launch (smallgemm.h) over those with
-// m <= 256; a launch with no items is skipped.
-template <typename T, typename TO>
-int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
-           const float* first, hipStream_t stream) {
-  const int64_t ts = plan.total[KIND_SYRK], ta = plan.total[KIND_APPLY];
-  const int64_t nu = plan.total[KIND_SMALL_UPPER], nr = plan.total[KIND_SMALL_RECT];
-  const int64_t gs = gemm_grid(ts), ga = gemm_grid(ta);
-  const dim3 gu((nu + 3) / 4), gr((nr + 3) / 4);
-  for (int t = 0; t < ns.iters; ++t) {
-    const int parity = t & 1;
-    const float* f = t == 0 ? first : nullptr;   // the Frobenius factor, first iteration only
-    const bool last = (t + 1 == ns.iters);
-    if (ts > 0) {
-      MO_TRY(launch(PK_SYRK, stream, [&] {
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                           dd, count, ts, parity, 0.f, 0.f, 0.f, f);
-      }));
-      MO_TRY(launch(PK_POLY, stream, [&] {
-        hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gs), dim3(NTHREADS), 0, stream,
-                           dd, count, plan.total[KIND_POLY], parity, ns.a, ns.b, ns.c, nullptr);
-      }));
-      MO_TRY(launch(PK_APPLY, stream, [&] {
-        if (last && ap.on)
-          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                             dd, count, ta, parity, ap.lr, 0.f, 0.f, f);
-        else if (last)
-          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                             dd, count, ta, parity, 0.f, 0.f, 0.f, f);
-        else
-          hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), dim3(ga), dim3(NTHREADS), 0, stream,
-                             dd, count, ta, parity, 0.f, 0.f, 0.f, f);
-      }));
-    }
-    if (nu > 0) {
-      MO_TRY(launch(PK_SYRK, stream, [&] {
-        hipLaunchKernelGGL((k_ns_small<T, GM_SYRK, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, 0.f,
-                           0.f, 0.f, f);
-      }));
-      MO_TRY(launch(PK_POLY, stream, [&] {
-        hipLaunchKernelGGL((k_ns_small<T, GM_POLY, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, ns.a,
-                           ns.b, ns.c, nullptr);
-      }));
-      MO_TRY(launch(PK_APPLY, stream, [&] {
-        if (last && ap.on)
-          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_WEIGHT, TO>), gr, dim3(256), 0, stream, dd, count, nr,
-                             parity, ap.lr, 0.f, 0.f, f);
-        else if (last)
-          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_FINAL, TO>), gr, dim3(256), 0, stream, dd, count, nr,
-                             parity, 0.f, 0.f, 0.f, f);
-        else
-          hipLaunchKernelGGL((k_ns_small<T, GM_APPLY, TO>), gr, dim3(256), 0, stream, dd, count, nr, parity,
-                             0.f, 0.f, 0.f, f);
-      }));
+// The second stream of a split call (see split_wanted), per device: created on
+// first use with the default priority, kept for the life of the process, with the
+// two events that fork it from the caller's stream and join it back.  `mu` is held
+// from the fork to the join, so calls from several threads do not interleave their
+// use of the events.
+struct SideStream {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+
+// This device's side stream, or nullptr if it is unavailable (creating it failed).
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> lock(ss.mu);
+  if (!ss.tried) {
+    ss.tried = true;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      if (ss.join) (void)hipEventDestroy(ss.join);
+      if (ss.fork) (void)hipEventDestroy(ss.fork);
+      if (ss.s) (void)hipStreamDestroy(ss.s);
+      ss.s = nullptr;
+      ss.fork = ss.join = nullptr;
+      (void)hipGetLastError();
     }
   }
-  return MO_OK;
+  return ss.s ? &ss : nullptr;
+}
+
+// Whether a call's NS products run as two halves on two streams.  Each launch of a
+// product deals its tiles to one block per CU in rounds; when a launch holds only a
+// few rounds, its last round leaves most CUs idle (1296 APPLY tiles over 256 CUs
+// are 5.06 rounds), and a second half running on another stream fills them.
+// Measured on one box, three rounds each: 125M-class owner set (5 APPLY rounds)
+// 1.95 -> 1.79-1.86 ms per step, 8 x 4096^2 orthogonalisation (8 rounds) 9.85-9.95
+// -> 9.29-9.30 ms, 1B-class set (49 rounds) -1%, 7B-class set (386 rounds) no gain;
+// three or four streams were slower.  Not under stream capture, and not for the
+// allocation-free call.
+constexpr int64_t SPLIT_MAX_ROUNDS = 16;
+bool split_wanted(const Plan& sizing, int count, const mo_ns_params& ns, hipStream_t stream) {
+  if (count < 2 || ns.iters < 1) return false;
+  const int64_t ta = sizing.total[KIND_APPLY];
+  const int64_t g = gemm_grid(std::numeric_limits<int32_t>::max());
+  if (ta == 0 || ta >= SPLIT_MAX_ROUNDS * g) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
+// k NS iterations: per product one persistent 256 x 256-tile launch over the
+// matrices with m > 256 and one 32 x 32-block launch (smallgemm.h) over those with
+// m <= 256; a launch with no items is skipped.  A split plan launches each
+// 256-tile product once per half: half A on the caller's stream, half B on the side
+// stream, forked after the first pass and joined before the call returns (the
+// small-path launches stay on the caller's stream).
+template <typename T, typename TO>
+int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
+           const float* first, hipStream_t stream, SideStream* side) {
+  const int64_t nu = plan.total[KIND_SMALL_UPPER], nr = plan.total[KIND_SMALL_RECT];
+  const dim3 gu((nu + 3) / 4), gr((nr + 3) / 4);
+  // the 256-tile launches of one half: descriptors, their count, item totals, stream
+  struct Half {
+    const MatDesc* dd;
+    int count;
+    int64_t ts, tp, ta;
+    hipStream_t stream;
+  };
+  Half halves[2];
+  int nh = 1;
+  const bool split = plan.split_at > 0 && side != nullptr;
+  if (split) {
+    halves[0] = {dd, plan.split_at, plan.half_total[0][0], plan.half_total[0][1], plan.half_total[0][2], stream};
+    halves[1] = {dd + plan.split_at, count - plan.split_at, plan.half_total[1][0], plan.half_total[1][1],
+                 plan.half_total[1][2], side->s};
+    nh = 2;
+  } else {
+    halves[0] = {dd, count, plan.total[KIND_SYRK], plan.total[KIND_POLY], plan.total[KIND_APPLY], stream};
+  }
+  std::unique_lock<std::mutex> lock;
+  if (split) {
+    lock = std::unique_lock<std::mutex>(side->mu);
+    if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return fail(MO_ERR_HIP, "forking the side stream failed");
+  }
+  auto products = [&]() -> int {
+    for (int t = 0; t < ns.iters; ++t) {
+      const int parity = t & 1;
+      const float* f = t == 0 ? first : nullptr;   // the Frobenius factor, first iteration only
+      const bool last = (t + 1 == ns.iters);
+      for (int h = 0; h < nh; ++h) {
+        const Half& H = halves[h];
+        if (H.ts == 0) continue;
+        MO_TRY(launch(PK_SYRK, H.stream, [&] {
+          hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gemm_grid(H.ts)), dim3(NTHREADS), 0, H.stream,
+                             H.dd, H.count, H.ts, parity, 0.f, 0.f, 0.f, f);
+        }));
+      }
+      for (int h = 0; h < nh; ++h) {
+        const Half& H = halves[h];
+        if (H.tp == 0) continue;
+        MO_TRY(launch(PK_POLY, H.stream, [&] {
+          hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gemm_grid(H.tp)), dim3(NTHREADS), 0, H.stream,
+                             H.dd, H.count, H.tp, parity, ns.a, ns.b, ns.c, nullptr);
+        }));
+      }
+      for (int h = 0; h < nh; ++h) {
+        const Half& H = halves[h];
+        if (H.ta == 0) continue;
+        const dim3 ga(gemm_grid(H.ta));
+        MO_TRY(launch(PK_APPLY, H.stream, [&] {
+          if (last && ap.on)
+            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), ga, dim3(NTHREADS), 0, H.stream,
+                               H.dd, H.count, H.ta, parity, ap.lr, 0.f, 0.f, f);
+          else if (last)
+            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), ga, dim3(NTHREADS), 0, H.stream,
+                               H.dd, H.count, H.ta, parity, 0.f, 0.f, 0.f, f);
+          else
+            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), ga, dim3(NTHREADS), 0, H.stream,
+                               H.dd, H.count, H.ta, parity, 0.f, 0.f, 0.f, f);
+        }));
+      }
+      if (nu > 0) {
+        MO_TRY(launch(PK_SYRK, stream, [&] {
+          hipLaunchKernelGGL((k_ns_small<T, GM_SYRK, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, 0.f,
+                             0.f, 0.f, f);
+        }));
+        MO_TRY(launch(PK_POLY, stream, [&] {
+          hipLaunchKernelGGL((k_ns_small<T, GM_POLY, TO>), gu, dim3(256), 0, stream, dd, count, nu, parity, ns.a,
+                             ns.b, ns.c, nullptr);
+        }));
+        MO_TRY(launch(PK_APPLY, stream, [&] {
+          if (last && ap.on)
+            hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_WEIGHT, TO>), gr, dim3(256), 0, stream, dd, count, nr,
+                               parity, ap.lr, 0.f, 0.f, f);
+          else if (last)
+            hipLaunchKernelGGL((k_ns_small<T, GM_APPLY_FINAL, TO>), gr, dim3(256), 0, stream, dd, count, nr,
+                               parity, 0.f, 0.f, 0.f, f);
+          else
+            hipLaunchKernelGGL((k_ns_small<T, GM_APPLY, TO>), gr, dim3(256), 0, stream, dd, count, nr, parity,
+                               0.f, 0.f, 0.f, f);
+        }));
+      }
+    }
+    return MO_OK;
+  };
+  const int rc = products();
+  if (split) {
+    // joined on every path, so no work of this call outlives it on the side stream
+    // unordered with the caller's later work
+    const bool ok = hipEventRecord(side->join, side->s) == hipSuccess &&
+                    hipStreamWaitEvent(stream, side->join, 0) == hipSuccess;
+    if (rc == MO_OK && !ok) return fail(MO_ERR_HIP, "joining the side stream failed");
+  }
+  return rc;
 }
 
 // Per-matrix device scalars and partial sums inside the workspace.
@@ -347,7 +477,7 @@ struct Scalars {
 // (gradient, or x for orthogonalise only); TC: compute; TO: output.
 template <typename TG, typename TC, typename TO>
 int run_step(const MatDesc* dd, int count, const Plan& plan, const Scalars& sc, bool momentum, float beta,
-             const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream) {
+             const mo_ns_params& ns, const ApplyOpt& ap, hipStream_t stream, SideStream* side) {
   // the NS source after the first pass: the fp32 momentum, or the input itself
   typedef typename std::conditional<std::is_same<TG, float>::value, float, bf16_t>::type TX;
   const int from_mom = momentum ? 1 : 0;
@@ -392,19 +522,20 @@ int run_step(const MatDesc* dd, int count, const Plan& plan, const Scalars& sc, 
       hipLaunchKernelGGL((k_prep_redo<TX, TC>), grid, dim3(256), 0, stream, dd, count, sc.scale, sc.redo,
                          from_mom);
   }));
-  return run_ns<TC, TO>(dd, count, plan, ns, ap, sc.first, stream);
+  return run_ns<TC, TO>(dd, count, plan, ns, ap, sc.first, stream, side);
 }
 
 template <typename TG>
 int dispatch_compute_out(const MatDesc* dd, int count, const Plan& plan, const Scalars& sc, bool momentum,
                          float beta, int compute, int out, const mo_ns_params& ns, const ApplyOpt& ap,
-                         hipStream_t stream) {
+                         hipStream_t stream, SideStream* side) {
   if (compute == MO_BF16) {
-    if (out == MO_BF16) return run_step<TG, bf16_t, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
-    return run_step<TG, bf16_t, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
+    if (out == MO_BF16)
+      return run_step<TG, bf16_t, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream, side);
+    return run_step<TG, bf16_t, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream, side);
   }
-  if (out == MO_BF16) return run_step<TG, float, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
-  return run_step<TG, float, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream);
+  if (out == MO_BF16) return run_step<TG, float, bf16_t>(dd, count, plan, sc, momentum, beta, ns, ap, stream, side);
+  return run_step<TG, float, float>(dd, count, plan, sc, momentum, beta, ns, ap, stream, side);
 }
 
 // Address of this device's copy of `scratch`, looked up once per device with that
@@ -481,9 +612,10 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   if (ws_bytes < plan.bytes)
     return fail(MO_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.bytes) + " bytes");
   unsigned char* base = static_cast<unsigned char*>(workspace);
-  Plan full;
-  MO_TRY(build_plan(mats, count, compute, momentum, base, full, in_dtype, out));
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  SideStream* side = (!noalloc && split_wanted(plan, count, *ns, stream)) ? side_stream() : nullptr;
+  Plan full;
+  MO_TRY(build_plan(mats, count, compute, momentum, base, full, in_dtype, out, side != nullptr));
   MatDesc* dd = reinterpret_cast<MatDesc*>(base + full.off_desc);
   Scalars sc;
   sc.scale = reinterpret_cast<float*>(base + full.off_scale);
@@ -493,8 +625,8 @@ int batched(const mo_matrix* mats, int count, int in_dtype, int compute, int out
   const NoEvents quiet(noalloc);
   MO_TRY(upload_by_args(dd, full.descs.data(), count, stream));
   if (in_dtype == MO_BF16)
-    return dispatch_compute_out<bf16_t>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
-  return dispatch_compute_out<float>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream);
+    return dispatch_compute_out<bf16_t>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream, side);
+  return dispatch_compute_out<float>(dd, count, full, sc, momentum, beta, compute, out, *ns, ap, stream, side);
 }
 
 }  // namespace

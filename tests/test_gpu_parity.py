@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from matrix_optimizers_sharded_amd.workloads import (
-    MUON_ABC, TEXTBOOK_QUINTIC_ABC, TEXTBOOK_CUBIC_ABC, BETA, EPS, WORKLOADS, host_matrix)
+    MUON_ABC, TEXTBOOK_QUINTIC_ABC, TEXTBOOK_CUBIC_ABC, BETA, EPS, WORKLOADS, host_matrix, f32_to_bf16_bits)
 from gpu_util import (say, to_dev_f32, to_dev_bf16, host_f32, rel_err, gaussian, bf16_round,
                       run_muon, run_ns)
 
@@ -350,6 +350,38 @@ def test_deterministic_and_batch_invariant(gpu):
         mi, ui = run([grads[i]], [moms[i]])
         np.testing.assert_array_equal(ui[0].view(np.uint32), u1[i].view(np.uint32))
         np.testing.assert_array_equal(mi[0].view(np.uint32), m1[i].view(np.uint32))
+
+
+def test_split_batch_follows_the_callers_stream(gpu):
+    """A batch with few rounds of tiles per launch runs its products as two halves,
+    one on the caller's stream and one on the library's second stream.  Inputs
+    written on the caller's stream right before the call (behind a spin kernel, so
+    they land late) must be what the second half reads, and the caller's next work
+    must see both halves' outputs."""
+    import torch
+    from matrix_optimizers_sharded_amd import muon_step_batched
+    shapes = [(768, 768), (768, 3072), (3072, 768), (768, 768), (512, 1024)]
+    grads = [bf16_round(gaussian(s, 800 + i, 0.02))[1] for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 900 + i, 0.02) for i, s in enumerate(shapes)]
+    m_ref, u_ref = run_muon(gpu, grads, moms, torch.bfloat16, torch.bfloat16, torch.bfloat16, BETA, MUON_ABC, 5,
+                            EPS)
+    g_src = [to_dev_bf16(f32_to_bf16_bits(g), gpu) for g in grads]
+    m_src = [to_dev_f32(m, gpu) for m in moms]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=gpu)
+    with torch.cuda.stream(s):
+        g_dev = [torch.zeros_like(t) for t in g_src]
+        m_dev = [torch.zeros_like(t) for t in m_src]
+        outs = [torch.zeros(sh, dtype=torch.bfloat16, device=gpu) for sh in shapes]
+        torch.cuda._sleep(50_000_000)
+        for d, t in zip(g_dev + m_dev, g_src + m_src):
+            d.copy_(t)
+        muon_step_batched(g_dev, m_dev, outs, BETA, *MUON_ABC, 5, EPS, compute=torch.bfloat16)
+        got = [o.clone() for o in outs]
+    s.synchronize()
+    for i in range(len(shapes)):
+        np.testing.assert_array_equal(host_f32(got[i]).view(np.uint32), u_ref[i].view(np.uint32))
+        np.testing.assert_array_equal(host_f32(m_dev[i]).view(np.uint32), m_ref[i].view(np.uint32))
 
 
 def test_tall_is_transpose_of_wide(gpu):
