@@ -46,7 +46,7 @@
  *     their Newton-Schulz products on a second stream of the library's own (one
  *     per device, created on first use with the default priority and kept for the
  *     life of the process): they do so when a product's launch holds fewer than
- *     16 rounds of 256x256 tiles per CU, not while `stream` is being captured
+ *     64 rounds of 256x256 tiles per CU, not while `stream` is being captured
  *     into a graph, and never in muon_step_batched_noalloc.  That stream waits
  *     for everything enqueued on `stream` before the call, and `stream` waits for
  *     it before anything enqueued after the call, so the ordering seen from

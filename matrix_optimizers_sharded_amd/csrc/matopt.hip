@@ -339,12 +339,13 @@ SideStream* side_stream() {
 // product deals its tiles to one block per CU in rounds; when a launch holds only a
 // few rounds, its last round leaves most CUs idle (1296 APPLY tiles over 256 CUs
 // are 5.06 rounds), and a second half running on another stream fills them.
-// Measured on one box, three rounds each: 125M-class owner set (5 APPLY rounds)
-// 1.95 -> 1.79-1.86 ms per step, 8 x 4096^2 orthogonalisation (8 rounds) 9.85-9.95
-// -> 9.29-9.30 ms, 1B-class set (49 rounds) -1%, 7B-class set (386 rounds) no gain;
+// Measured on one box, two or three rounds each: 125M-class owner set (5 APPLY
+// rounds) 2.15-2.17 -> 2.04-2.05 ms per step, 8 x 4096^2 orthogonalisation (8
+// rounds) 9.96-10.03 -> 9.48 ms, 1B-class set (49 rounds) 29.53-29.62 -> 29.05-29.25
+// ms; as two calls from Python the 7B-class set (386 rounds) gained nothing, and
 // three or four streams were slower.  Not under stream capture, and not for the
 // allocation-free call.
-constexpr int64_t SPLIT_MAX_ROUNDS = 16;
+constexpr int64_t SPLIT_MAX_ROUNDS = 64;
 bool split_wanted(const Plan& sizing, int count, const mo_ns_params& ns, hipStream_t stream) {
   if (count < 2 || ns.iters < 1) return false;
   const int64_t ta = sizing.total[KIND_APPLY];
