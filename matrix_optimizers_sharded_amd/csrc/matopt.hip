@@ -369,7 +369,7 @@ template <typename T, typename TO>
 int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& ns, const ApplyOpt& ap,
            const float* first, hipStream_t stream, SideStream* side) {
   const int64_t nu = plan.total[KIND_SMALL_UPPER], nr = plan.total[KIND_SMALL_RECT];
-  const dim3 gu((nu + 3) / 4), gr((nr + 3) / 4);
+  const dim3 gu(nu), gr(nr);   // one 32 x 32 block per 256-thread block
   // the 256-tile launches of one half: descriptors, their count, item totals, stream
   struct Half {
     const MatDesc* dd;

@@ -41,7 +41,10 @@ __device__ inline void small_upper(int64_t local, int t, int& bi, int& bj) {
   bj = r + static_cast<int>(local);
 }
 
-// One 32 x 32 block per wave, 4 waves per 256-thread block.
+// One 32 x 32 block per 256-thread block: each of its 4 waves (one per SIMD) takes a
+// quarter of the k steps, waves 1-3 leave their partial sums in LDS, and wave 0 adds
+// them in wave order and writes the block.  (With one block per wave, the whole k
+// range was one chain of dependent MFMAs on one SIMD.)
 //   SYRK   C = alpha X X^T (upper blocks, mirrored), K = n
 //   POLY   C = aI + b A + c A A (upper blocks, mirrored), K = m
 //   APPLY  X' = alpha B' X (all blocks), K = m; the last one writes U or W - lr U
@@ -53,9 +56,10 @@ __global__ __launch_bounds__(256) void k_ns_small(const MatDesc* __restrict__ de
   constexpr int kind = SYM ? KIND_SMALL_UPPER : KIND_SMALL_RECT;
   constexpr int KB = ROW_BYTES / static_cast<int>(sizeof(T));   // elements per k-block
   constexpr int KSTEP = sizeof(T) == 2 ? 16 : 8;                 // k per MFMA step (both lane halves)
-  const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (item >= total) return;   // whole waves only: no barrier below
+  __shared__ float partial[3][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t item = blockIdx.x;
+  if (item >= total) return;   // the whole block (the grid holds `total` blocks)
   const int di = find_desc(descs, count, kind, item);
   const MatDesc& d = descs[di];
   const int64_t local = item - d.begin[kind];
@@ -89,6 +93,8 @@ __global__ __launch_bounds__(256) void k_ns_small(const MatDesc* __restrict__ de
     K = d.m;
   }
   const int steps = (K + KSTEP - 1) / KSTEP;
+  // this wave's quarter of the k steps
+  const int s_begin = steps * wave / 4, s_end = steps * (wave + 1) / 4;
   typedef typename Mfma<T>::frag frag_t;
   // first operand: row i0 + l32, the 16 bytes of k at chunk c = 2 (s % 4) + half of
   // k-block s / 4 (the fragment layout of gemm.h, read from the workspace directly)
@@ -113,9 +119,12 @@ __global__ __launch_bounds__(256) void k_ns_small(const MatDesc* __restrict__ de
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  constexpr int U = 4;   // steps whose loads go out together
-  int s = 0;
-  for (; s + U <= steps; s += U) {
+  // steps whose loads go out together: 16 took APPLY on a 256 x 128 fp32 matrix
+  // from 17.9 to 9.8 us per launch against 4 (its second operand arrives element by
+  // element); SYRK and POLY, whose operands are 16-byte loads, did not change
+  constexpr int U = 16;
+  int s = s_begin;
+  for (; s + U <= s_end; s += U) {
     frag_t a[U], b[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -125,11 +134,21 @@ __global__ __launch_bounds__(256) void k_ns_small(const MatDesc* __restrict__ de
 #pragma unroll
     for (int u = 0; u < U; ++u) Mfma<T>::mma(acc, a[u], b[u]);
   }
-  for (; s < steps; ++s) {
+  for (; s < s_end; ++s) {
     const frag_t a = frag_rows(P, pP, i0 + l32, s);
     const frag_t b = SYM ? frag_rows(Q, pQ, j0 + l32, s) : frag_cols(s);
     Mfma<T>::mma(acc, a, b);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) partial[wave - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += partial[w][r][lane];
 
   float alpha = 1.f;
   if (MODE != GM_POLY && first != nullptr) {
