@@ -384,6 +384,60 @@ def test_split_batch_follows_the_callers_stream(gpu):
         np.testing.assert_array_equal(host_f32(m_dev[i]).view(np.uint32), m_ref[i].view(np.uint32))
 
 
+def test_split_batches_from_two_threads(gpu):
+    """Two host threads, each with its own torch stream, call the split path at the
+    same time (ctypes releases the GIL, and both calls share the library's second
+    stream and its fork/join events): every call's results equal the same batch run
+    alone."""
+    import threading
+    import torch
+    from matrix_optimizers_sharded_amd import muon_step_batched
+    sets = [[(768, 768), (768, 2048), (1024, 512)], [(512, 1536), (768, 768), (640, 1280)]]
+    inputs, refs = [], []
+    for t, shapes in enumerate(sets):
+        grads = [bf16_round(gaussian(s, 1400 + 10 * t + i, 0.02))[1] for i, s in enumerate(shapes)]
+        moms = [gaussian(s, 1500 + 10 * t + i, 0.02) for i, s in enumerate(shapes)]
+        inputs.append((shapes, grads, moms))
+        refs.append(run_muon(gpu, grads, moms, torch.bfloat16, torch.bfloat16, torch.bfloat16, BETA, MUON_ABC, 5,
+                             EPS))
+    got, errors = {}, []
+
+    def worker(t):
+        try:
+            shapes, grads, moms = inputs[t]
+            s = torch.cuda.Stream(device=gpu)
+            with torch.cuda.stream(s):
+                g_dev = [to_dev_bf16(f32_to_bf16_bits(g), gpu) for g in grads]
+                m0 = [to_dev_f32(m, gpu) for m in moms]
+                m_dev = [torch.empty_like(m) for m in m0]
+                outs = [torch.empty(sh, dtype=torch.bfloat16, device=gpu) for sh in shapes]
+                runs = []
+                for _ in range(4):
+                    for m, m_init in zip(m_dev, m0):
+                        m.copy_(m_init)
+                    muon_step_batched(g_dev, m_dev, outs, BETA, *MUON_ABC, 5, EPS, compute=torch.bfloat16)
+                    runs.append(([o.clone() for o in outs], [m.clone() for m in m_dev]))
+            s.synchronize()
+            got[t] = [([host_f32(o) for o in us], [host_f32(m) for m in ms]) for us, ms in runs]
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(len(sets))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(len(sets)):
+        m_ref, u_ref = refs[t]
+        for r, (us, ms) in enumerate(got[t]):
+            for i in range(len(sets[t])):
+                np.testing.assert_array_equal(us[i].view(np.uint32), u_ref[i].view(np.uint32),
+                                              err_msg=f"thread {t} call {r} matrix {i}: U")
+                np.testing.assert_array_equal(ms[i].view(np.uint32), m_ref[i].view(np.uint32),
+                                              err_msg=f"thread {t} call {r} matrix {i}: momentum")
+
+
 def test_tall_is_transpose_of_wide(gpu):
     import torch
     g = gaussian((200, 520), 5)
