@@ -571,10 +571,6 @@ template <typename T> __device__ inline uint32_t bits_of(T v) {
   if constexpr (sizeof(T) == 4) return __float_as_uint(v);
   else return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, v));
 }
-template <typename T> __device__ inline T of_bits(uint32_t b) {
-  if constexpr (sizeof(T) == 4) return __uint_as_float(b);
-  else return __builtin_bit_cast(bf16_t, static_cast<uint16_t>(b));
-}
 // element k of a 16-byte piece as fp32, and the piece with element k replaced
 template <typename T> __device__ inline float piece_get(const u32x4_t& v, int k) {
   if constexpr (sizeof(T) == 4) return __uint_as_float(v[k]);
