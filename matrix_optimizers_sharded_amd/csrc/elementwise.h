@@ -363,8 +363,14 @@ __global__ __launch_bounds__(256) void k_scaled_copy(const MatDesc* __restrict__
 // ---------------------------------------------------------------------------
 // Sign-Muon tail.
 
-constexpr int UNPACK_PIECES = 4;
-constexpr int SAPPLY_PIECES = 2;
+// 16-byte pieces per lane (see below).  Measured at 2^28 elements, each kernel
+// timed right after the others in a pack/vote/unpack/apply loop, three rounds on
+// one box: sign_unpack (bf16 out) 1 piece 7.09-7.19 TB/s, 2 pieces 5.97-6.09,
+// 4 pieces 5.92-6.05, 8 pieces 5.63-5.73; sign_apply (fp32 weight) 1 piece
+// 6.49-6.54, 2 pieces 6.18-6.22, 4 pieces 6.13-6.17.  sign_pack (below) wants 2
+// loads per lane: 6.45-6.52 TB/s against 5.19-5.21 with 1.
+constexpr int UNPACK_PIECES = 1;
+constexpr int SAPPLY_PIECES = 1;
 
 // sign_pack: each lane of a wave reads PACK_LOADS 16-byte pieces (4 fp32 or 8 bf16
 // elements each), the 64 lanes of one load on 64 consecutive pieces, so that every
