@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MATOPT_VERSION 111
+#define MATOPT_VERSION 112
 
 /* element types */
 enum { MO_F32 = 0, MO_BF16 = 1 };
@@ -247,6 +247,10 @@ typedef struct {
   char name[32];     /* kernel kind, e.g. "ns_syrk"                               */
   int64_t launches;  /* launches recorded                                          */
   double total_ms;   /* sum of event-measured durations                            */
+  double busy_ms;    /* time with at least one launch of this kind running: the
+                        union of their event intervals on one timeline (equal to
+                        total_ms when they never overlap; when the records span
+                        more than one device, total_ms)                          */
 } mo_kernel_time;
 
 int32_t mo_profile_begin(void);

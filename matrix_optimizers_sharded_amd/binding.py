@@ -32,7 +32,8 @@ class MoNsParams(ctypes.Structure):
 
 
 class MoKernelTime(ctypes.Structure):
-    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("busy_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -424,10 +425,12 @@ def profile_begin():
 
 
 def profile_end():
-    """Per-kernel-kind {name: (launches, total_ms)} since profile_begin()."""
+    """Per-kernel-kind {name: (launches, total_ms, busy_ms)} since profile_begin():
+    busy_ms is the union of the launches' intervals (less than total_ms when launches
+    of a kind overlap, as the two halves of a split product do)."""
     lib = load_library()
     buf = (MoKernelTime * 32)()
     n = lib.mo_profile_end(buf, 32)
     if n < 0:
         _check(n)
-    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 32))}
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms, buf[i].busy_ms) for i in range(min(n, 32))}

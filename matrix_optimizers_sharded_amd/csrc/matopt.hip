@@ -808,13 +808,26 @@ int32_t mo_profile_end(mo_kernel_time* out, int32_t max) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
   double ms[PK_N] = {0};
   int64_t n[PK_N] = {0};
+  // each launch as [start, end) in ms after the first record's start event, for
+  // the union per kind; `one_timeline` turns false if an offset cannot be taken
+  // (events of another device)
+  std::vector<std::pair<double, double>> iv[PK_N];
+  bool one_timeline = true;
   int rc = MO_OK;
+  const hipEvent_t ref = g_prof_recs.empty() ? nullptr : g_prof_recs.front().e0;
   for (const ProfRec& r : g_prof_recs) {
-    float t = 0.f;
+    float t = 0.f, off = 0.f;
     if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess)
       rc = fail(MO_ERR_HIP, "event timing failed");
+    if (one_timeline && hipEventElapsedTime(&off, ref, r.e0) != hipSuccess) {
+      one_timeline = false;
+      (void)hipGetLastError();
+    }
     ms[r.kind] += t;
     n[r.kind] += 1;
+    iv[r.kind].emplace_back(off, off + t);
+  }
+  for (const ProfRec& r : g_prof_recs) {
     g_ev_pool.push_back(r.e0);
     g_ev_pool.push_back(r.e1);
   }
@@ -823,11 +836,28 @@ int32_t mo_profile_end(mo_kernel_time* out, int32_t max) {
   int k = 0;
   for (int i = 0; i < PK_N; ++i) {
     if (!n[i]) continue;
+    double busy = ms[i];
+    if (one_timeline) {
+      std::sort(iv[i].begin(), iv[i].end());
+      busy = 0.0;
+      double s0 = iv[i].front().first, e0 = iv[i].front().second;
+      for (const auto& x : iv[i]) {
+        if (x.first > e0) {
+          busy += e0 - s0;
+          s0 = x.first;
+          e0 = x.second;
+        } else if (x.second > e0) {
+          e0 = x.second;
+        }
+      }
+      busy += e0 - s0;
+    }
     if (out && k < max) {
       std::memset(&out[k], 0, sizeof(mo_kernel_time));
       std::strncpy(out[k].name, kKindNames[i], sizeof(out[k].name) - 1);
       out[k].launches = n[i];
       out[k].total_ms = ms[i];
+      out[k].busy_ms = busy;
     }
     ++k;
   }

@@ -438,6 +438,36 @@ def test_split_batches_from_two_threads(gpu):
                                               err_msg=f"thread {t} call {r} matrix {i}: momentum")
 
 
+def test_profile_busy_time_merges_overlapping_halves(gpu):
+    """mo_profile_end's busy time is the union of a kind's launch intervals: for the
+    products of a split batch (two halves on two streams) it lies between the longest
+    single launch and the sum of all of them; for kinds launched once per step on one
+    stream it equals the sum."""
+    import torch
+    import matrix_optimizers_sharded_amd as mo
+    shapes = [(768, 768), (768, 3072), (3072, 768), (768, 768)]
+    grads = [to_dev_bf16(f32_to_bf16_bits(bf16_round(gaussian(s, 1600 + i, 0.02))[1]), gpu)
+             for i, s in enumerate(shapes)]
+    moms = [to_dev_f32(gaussian(s, 1700 + i, 0.02), gpu) for i, s in enumerate(shapes)]
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=gpu) for s in shapes]
+    ws = mo.Workspace(gpu)
+    mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, 5, EPS, workspace=ws)
+    torch.cuda.synchronize()
+    mo.profile_begin()
+    for _ in range(3):
+        mo.muon_step_batched(grads, moms, outs, BETA, *MUON_ABC, 5, EPS, workspace=ws)
+    torch.cuda.synchronize()
+    k = mo.profile_end()
+    say(f"profile: {k}")
+    for name in ("ns_syrk", "ns_poly", "ns_apply"):
+        launches, total, busy = k[name]
+        assert launches == 3 * 5 * 2, (name, launches)          # 3 calls x 5 iterations x 2 halves
+        assert busy <= total * (1 + 1e-6), (name, busy, total)
+        assert busy >= total / launches, (name, busy, total)
+    launches, total, busy = k["momentum_prep"]
+    assert launches == 3 and abs(busy - total) <= 1e-3 * total, (busy, total)
+
+
 def test_tall_is_transpose_of_wide(gpu):
     import torch
     g = gaussian((200, 520), 5)
