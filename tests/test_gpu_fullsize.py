@@ -17,7 +17,7 @@ import scipy.linalg
 import oracle
 from matrix_optimizers_sharded_amd.workloads import (
     MUON_ABC, BETA, EPS, WORKLOADS, host_matrix, device_matrix, f32_to_bf16_bits)
-from gpu_util import say, to_dev_f32, to_dev_bf16, host_f32, rel_err
+from gpu_util import say, to_dev_f32, to_dev_bf16, host_f32, rel_err, gaussian, bf16_round
 from pins import scalar_poly_iterate
 
 pytestmark = pytest.mark.gpu
@@ -160,6 +160,50 @@ def test_1b_class_swiglu_fp32_compute(gpu):
 def test_7b_class_owner_set(gpu):
     # 4096^2, 4096x11008, 11008x4096 from layer 0, and the last matrix of layer 31
     check_owner_set(4, [0, 4, 6, 223], gpu, spectrum=[0, 6])
+
+
+@pytest.mark.timeout(1200)
+def test_7b_class_fused_weight_update(gpu):
+    """muon_step_apply over the whole 7B-class set with bf16 weights, as the fused-
+    update benchmark runs it: on sampled matrices each new weight is within half a
+    bf16 ulp of the exact W - lr U plus lr times the direction's bf16-path error, and
+    the momentum equals the exact fused multiply-add."""
+    import torch
+    from matrix_optimizers_sharded_amd import muon_step_apply
+    wid, sample, lr = 4, [0, 6], 0.05
+    w = WORKLOADS[wid]
+    grads, moms, weights, host = [], [], [], {}
+    for i in range(w.count):
+        if i in sample:
+            d = host_matrix(wid, i)
+            wb, d["w0"] = bf16_round(gaussian(d["shape"], 3000 + i, 0.02))
+            host[i] = d
+            grads.append(to_dev_bf16(d["grad_bits"], gpu))
+            moms.append(to_dev_f32(d["mom"], gpu))
+            weights.append(to_dev_bf16(wb, gpu))
+        else:
+            g, m = device_matrix(wid, i, gpu)
+            grads.append(g)
+            moms.append(m)
+            weights.append((torch.randn(w.shapes[i], device=gpu) * 0.02).to(torch.bfloat16))
+    say(f"{w.name}: {w.count} matrices and bf16 weights resident, one fused step")
+    muon_step_apply(grads, moms, weights, BETA, *MUON_ABC, w.iters, lr, EPS, compute=torch.bfloat16)
+    torch.cuda.synchronize()
+    for i in sample:
+        d = host[i]
+        say(f"{w.name}: oracle on matrix {i} {d['shape']}")
+        want_m, u = oracle.muon_step(d["grad"], d["mom"], BETA, *MUON_ABC, w.iters, EPS)
+        np.testing.assert_array_equal(host_f32(moms[i]).view(np.uint32), want_m.view(np.uint32))
+        want = oracle.weight_update(d["w0"], u, lr)
+        got = host_f32(weights[i]).astype(np.float64)
+        half_ulp = np.abs(want) * 2.0 ** -8 + 1e-30          # bf16 has 8 significant bits
+        resid = np.linalg.norm(np.maximum(np.abs(got - want) - half_ulp, 0.0))
+        bound = float(np.float32(lr)) * 2e-2 * np.linalg.norm(u)
+        say(f"{w.name}: matrix {i} excess over half an ulp {resid:.3e} (bound {bound:.3e})")
+        assert resid <= bound, (i, resid, bound)
+    del grads, moms, weights
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
