@@ -1,0 +1,45 @@
+"""The C ABI from plain C++: tests/c_abi/abi_step.cpp (HIP runtime only, no Python or
+torch in its process) runs a batched step on three matrices that take both product
+paths, packs one result's signs, and checks an argument error and the version.  Its
+results are compared here with the fp64 oracle on the inputs it wrote: the momentum
+bit-exact, U within the fp32 bar, the packed signs bit-exact."""
+
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from matrix_optimizers_sharded_amd.workloads import MUON_ABC, BETA, EPS
+from gpu_util import say, rel_err
+
+pytestmark = pytest.mark.gpu
+
+BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "abi_step")
+SHAPES = [(300, 200), (512, 768), (768, 512)]
+# the values abi_step.cpp passes
+ABC, ITERS, BETA_C, EPS_C = (3.4445, -4.775, 2.0315), 5, 0.95, 1e-7
+
+
+def test_step_through_the_c_abi_from_cpp(gpu):
+    assert (tuple(MUON_ABC), BETA, EPS) == (ABC, BETA_C, EPS_C), "abi_step.cpp's constants drifted"
+    assert os.path.exists(BIN), "tests/c_abi/abi_step is not built: run __graft_entry__.build()"
+    with tempfile.TemporaryDirectory() as d:
+        res = subprocess.run([BIN, d], capture_output=True, text=True, timeout=120)
+        say(res.stdout.strip())
+        assert res.returncode == 0, res.stdout + res.stderr
+        u_all = []
+        for i, (r, c) in enumerate(SHAPES):
+            def load(name):
+                return np.fromfile(os.path.join(d, f"{name}{i}.f32"), dtype=np.float32).reshape(r, c)
+            g, m, m_new, u = load("g"), load("m"), load("mnew"), load("u")
+            want_m, want_u = oracle.muon_step(g, m, BETA, *MUON_ABC, ITERS, EPS)
+            np.testing.assert_array_equal(m_new.view(np.uint32), want_m.view(np.uint32))
+            err = rel_err(u, want_u)
+            say(f"C++ caller, {r}x{c}: rel err {err:.3e}")
+            assert err <= 1e-4, (i, err)
+            u_all.append(u)
+        packed = np.fromfile(os.path.join(d, "packed1.u32"), dtype=np.uint32)
+        np.testing.assert_array_equal(packed, oracle.sign_pack(u_all[1]))
