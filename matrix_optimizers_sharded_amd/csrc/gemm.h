@@ -342,7 +342,14 @@ struct TileRef {
 // slabs of a tile start the loads of the next tile's first slabs, so those land while
 // this tile finishes and writes its epilogue, and no tile pays a cold start.  (A
 // shared work queue fed by an atomic counter measured about 1% slower.)
-template <typename T, int MODE, typename TO>
+// SMALLK (bf16 operands only) is chosen by the host for launches whose matrices all
+// have m <= 2048, where a tile holds at most 32 k-slabs and its fixed costs weigh
+// more: a diagonal SYRK / POLY tile, whose two operands are the same row panel,
+// loads that panel once and reads both operands' fragments from it, and APPLY sends
+// its rows out through the epilogue staging slab as whole 1 KiB runs.  Both were
+// measured slower at the 7B-class set (m = 4096), which keeps the plain kernel.
+constexpr int SMALLK_MAX_M = 2048;
+template <typename T, int MODE, typename TO, bool SMALLK = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
 void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int parity, float ca, float cb,
                float cc, const float* __restrict__ first) {
@@ -379,6 +386,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // rows of k-block (NWAVES q + w) / RG, from row ((NWAVES q + w) % RG) * 8.
   constexpr bool QT = MODE == GM_APPLY || MODE == GM_APPLY_FINAL || MODE == GM_APPLY_WEIGHT;
   constexpr bool EARLY_P = MODE == GM_POLY;   // POLY: P loads before the last step's MFMAs
+  static_assert(!SMALLK || sizeof(T) == 2, "the SMALLK kernel is for bf16 operands");
+  constexpr bool ONE_PANEL = SMALLK && SYM;    // diagonal tiles load P only
   constexpr int KB = ROW_BYTES / static_cast<int>(sizeof(T));   // elements per k-block
   constexpr int KR = KB;                                         // k rows per slab
   constexpr int JB = GT / KB;                                    // k-blocks per tile width
@@ -468,7 +477,12 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   };
   auto issue = [&](const TileRef& t, int kt, int stage) {
     issue_op(t, kt, stage, 0);
-    issue_op(t, kt, stage, 1);
+    if (!(ONE_PANEL && t.diag)) issue_op(t, kt, stage, 1);
+  };
+  // where the second operand sits in a stage: P's own half for a diagonal tile
+  // that loads one panel
+  auto q_off = [&](const TileRef& t) {
+    return (ONE_PANEL && t.diag) ? 0u : static_cast<uint32_t>(OPERAND_BYTES);
   };
 
   f32x16_t acc[4][NB];
@@ -536,10 +550,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // the fragments of k16 step kk of the stage at sP that a wave of diagonal class D
   // uses (every fragment for D = 3)
-  auto read_frags = [&](auto dtag, const unsigned char* sP, int kk, frag_t* A, frag_t* B) {
+  auto read_frags = [&](auto dtag, const unsigned char* sP, uint32_t qoff, int kk, frag_t* A, frag_t* B) {
     constexpr int D = decltype(dtag)::value;
     constexpr int NA = a_needed(D), B0 = b_first(D);
-    const unsigned char* sQ = sP + OPERAND_BYTES;
+    const unsigned char* sQ = sP + (ONE_PANEL ? qoff : static_cast<uint32_t>(OPERAND_BYTES));
     const int c = 2 * kk + half;
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -608,9 +622,14 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
   // prologue: slabs 0..NSTAGE-1 of the first tile (every tile has more slabs)
 #pragma unroll
   for (int sidx = 0; sidx < NSTAGE; ++sidx) issue(cur, sidx, sidx);
-  wait_loads(NSTAGE - 1);
+  // slab 0 landed: one slab's loads may still be in flight, unless a diagonal first
+  // tile loaded one panel, where that count would also cover slab 0's
+  if (ONE_PANEL && cur.diag)
+    wait_loads(0);
+  else
+    wait_loads(NSTAGE - 1);
   __syncthreads();
-  read_frags(IC<3>{}, smem, 0, fa[0], fb[0]);
+  read_frags(IC<3>{}, smem, q_off(cur), 0, fa[0], fb[0]);
   int stage = 0;
   // The k-loop of one tile for a wave of diagonal class D (3 off the diagonal).
   auto kloop = [&](auto dtag) {
@@ -622,7 +641,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       const unsigned char* sP = smem + stage * STAGE_BYTES;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS - 1; ++kk) {
-        read_frags(dtag, sP, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        read_frags(dtag, sP, q_off(cur), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
         mfma_step(dtag, fa[kk & 1], fb[kk & 1]);
         interleave(IC<NR_IN>{}, IC<NM>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -643,13 +662,13 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       if (EARLY_P && load) issue_op(lt, lk, stage, 0);
       // the next slab's first fragments, of this tile or (last slab) the next one:
       // all of them, whatever the next tile's class
-      read_frags(IC<3>{}, smem + next * STAGE_BYTES, 0, fa[0], fb[0]);
+      read_frags(IC<3>{}, smem + next * STAGE_BYTES, q_off(kt + 1 < cur.nk ? cur : nxt), 0, fa[0], fb[0]);
       mfma_step(dtag, fa[(KSTEPS - 1) & 1], fb[(KSTEPS - 1) & 1]);
       interleave(IC<NR_NEXT>{}, IC<NM>{});
       __builtin_amdgcn_sched_barrier(0);
       if (load) {
         if (!EARLY_P) issue_op(lt, lk, stage, 0);
-        issue_op(lt, lk, stage, 1);
+        if (!(ONE_PANEL && lt.diag)) issue_op(lt, lk, stage, 1);
       }
       stage = next;
     }
@@ -742,6 +761,32 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           return e;
         };
         unsigned char* stg = staging + wave * 4096;
+        if constexpr (SMALLK && MODE == GM_APPLY) {
+          // X' through the staging slab: the wave's 64 columns are one 128-byte
+          // k-block row, so a round of 32 rows (one MFMA row block) goes out as 4
+          // stores of 8 whole rows (1 KiB contiguous) each
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const int r = 8 * g + 4 * half + t;        // row within the round
+                  const int off = (b * 32 + l32) * 2;        // byte within the row
+                  *reinterpret_cast<T*>(stg + r * 128 + ((((off >> 4) ^ (r & 7)) << 4) | (off & 15))) =
+                      from_f32<T>(acc[a][b][4 * g + t] * alpha);
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = (lane >> 3) + 8 * q, c = lane & 7;
+              const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ (r & 7)) << 4));
+              store_ws(at<u32x4_t>(Cr, kb_off<T>(i0 + wm + a * 32 + r, j0 + wn + c * 8, pr)), w);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // rounds one after another
+          }
+        } else
 #pragma unroll
         for (int p = 0; p < 4 / AP; ++p)
 #pragma unroll

@@ -95,6 +95,9 @@ struct Plan {
   // half_total[h][kind] counts them (the other kinds number across the whole table).
   int split_at = 0;
   int64_t half_total[2][3] = {};
+  // the largest m among the 256-tile matrices of each half (of the whole list in
+  // [0] when it is not split): it picks the GEMM kernel variant
+  int32_t max_m[2] = {0, 0};
 };
 // the GEMM kinds a split plan numbers per half
 bool per_half_kind(int kd) { return kd == KIND_SYRK || kd == KIND_POLY || kd == KIND_APPLY; }
@@ -202,6 +205,7 @@ int build_plan(const mo_matrix* mats, int count, int compute, bool momentum, uns
     d.items[KIND_PREP] = (int64_t(d.mp) / PREP_TILE) * (int64_t(d.np) / PREP_TILE);
     d.items[KIND_CHUNK] = (d.numel + CHUNK - 1) / CHUNK;
     const int h = (plan.split_at > 0 && k >= plan.split_at) ? 1 : 0;
+    if (d.items[KIND_APPLY] > 0) plan.max_m[h] = std::max(plan.max_m[h], d.m);
     for (int kd = 0; kd < NKIND; ++kd) {
       if (plan.split_at > 0 && per_half_kind(kd)) {
         d.begin[kd] = plan.half_total[h][kd - KIND_SYRK];
@@ -376,18 +380,36 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
     int count;
     int64_t ts, tp, ta;
     hipStream_t stream;
+    bool smallk;   // bf16 operands and every matrix m <= SMALLK_MAX_M (gemm.h)
   };
   Half halves[2];
   int nh = 1;
   const bool split = plan.split_at > 0 && side != nullptr;
   if (split) {
-    halves[0] = {dd, plan.split_at, plan.half_total[0][0], plan.half_total[0][1], plan.half_total[0][2], stream};
+    halves[0] = {dd, plan.split_at, plan.half_total[0][0], plan.half_total[0][1], plan.half_total[0][2], stream,
+                 false};
     halves[1] = {dd + plan.split_at, count - plan.split_at, plan.half_total[1][0], plan.half_total[1][1],
-                 plan.half_total[1][2], side->s};
+                 plan.half_total[1][2], side->s, false};
     nh = 2;
   } else {
-    halves[0] = {dd, count, plan.total[KIND_SYRK], plan.total[KIND_POLY], plan.total[KIND_APPLY], stream};
+    halves[0] = {dd, count, plan.total[KIND_SYRK], plan.total[KIND_POLY], plan.total[KIND_APPLY], stream, false};
   }
+  for (int h = 0; h < nh; ++h) halves[h].smallk = sizeof(T) == 2 && plan.max_m[h] <= SMALLK_MAX_M;
+  // one 256-tile product launch of one half, in the kernel variant the half takes
+  auto gemm = [&](auto mode, const Half& H, int64_t items, int parity, float ca, float cb, float cc,
+                  const float* f) {
+    constexpr int M = decltype(mode)::value;
+    const dim3 grid(gemm_grid(items));
+    if constexpr (sizeof(T) == 2) {
+      if (H.smallk) {
+        hipLaunchKernelGGL((k_ns_gemm<T, M, TO, true>), grid, dim3(NTHREADS), 0, H.stream, H.dd, H.count, items,
+                           parity, ca, cb, cc, f);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((k_ns_gemm<T, M, TO, false>), grid, dim3(NTHREADS), 0, H.stream, H.dd, H.count, items,
+                       parity, ca, cb, cc, f);
+  };
   std::unique_lock<std::mutex> lock;
   if (split) {
     lock = std::unique_lock<std::mutex>(side->mu);
@@ -402,33 +424,23 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
       for (int h = 0; h < nh; ++h) {
         const Half& H = halves[h];
         if (H.ts == 0) continue;
-        MO_TRY(launch(PK_SYRK, H.stream, [&] {
-          hipLaunchKernelGGL((k_ns_gemm<T, GM_SYRK, TO>), dim3(gemm_grid(H.ts)), dim3(NTHREADS), 0, H.stream,
-                             H.dd, H.count, H.ts, parity, 0.f, 0.f, 0.f, f);
-        }));
+        MO_TRY(launch(PK_SYRK, H.stream, [&] { gemm(IC<GM_SYRK>{}, H, H.ts, parity, 0.f, 0.f, 0.f, f); }));
       }
       for (int h = 0; h < nh; ++h) {
         const Half& H = halves[h];
         if (H.tp == 0) continue;
-        MO_TRY(launch(PK_POLY, H.stream, [&] {
-          hipLaunchKernelGGL((k_ns_gemm<T, GM_POLY, TO>), dim3(gemm_grid(H.tp)), dim3(NTHREADS), 0, H.stream,
-                             H.dd, H.count, H.tp, parity, ns.a, ns.b, ns.c, nullptr);
-        }));
+        MO_TRY(launch(PK_POLY, H.stream, [&] { gemm(IC<GM_POLY>{}, H, H.tp, parity, ns.a, ns.b, ns.c, nullptr); }));
       }
       for (int h = 0; h < nh; ++h) {
         const Half& H = halves[h];
         if (H.ta == 0) continue;
-        const dim3 ga(gemm_grid(H.ta));
         MO_TRY(launch(PK_APPLY, H.stream, [&] {
           if (last && ap.on)
-            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_WEIGHT, TO>), ga, dim3(NTHREADS), 0, H.stream,
-                               H.dd, H.count, H.ta, parity, ap.lr, 0.f, 0.f, f);
+            gemm(IC<GM_APPLY_WEIGHT>{}, H, H.ta, parity, ap.lr, 0.f, 0.f, f);
           else if (last)
-            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY_FINAL, TO>), ga, dim3(NTHREADS), 0, H.stream,
-                               H.dd, H.count, H.ta, parity, 0.f, 0.f, 0.f, f);
+            gemm(IC<GM_APPLY_FINAL>{}, H, H.ta, parity, 0.f, 0.f, 0.f, f);
           else
-            hipLaunchKernelGGL((k_ns_gemm<T, GM_APPLY, TO>), ga, dim3(NTHREADS), 0, H.stream,
-                               H.dd, H.count, H.ta, parity, 0.f, 0.f, 0.f, f);
+            gemm(IC<GM_APPLY>{}, H, H.ta, parity, 0.f, 0.f, 0.f, f);
         }));
       }
       if (nu > 0) {
