@@ -25,7 +25,9 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 KINDS = [
-    # rocprofv3 prints some names mangled (bf16 arguments) and some demangled
+    # Mangled and demangled names are both recognised.  The profiling commands pass
+    # --mangled-kernels: rocprofv3's demangler turns some bf16 instantiations into
+    # text that no longer shows their template arguments.
     (re.compile(r"k_ns_(gemm|small)(I.*Li0E|<[^,]+, 0,)"), "ns_syrk"),
     (re.compile(r"k_ns_(gemm|small)(I.*Li1E|<[^,]+, 1,)"), "ns_poly"),
     (re.compile(r"k_ns_(gemm|small)(I.*Li[234]E|<[^,]+, [234],)"), "ns_apply"),
@@ -73,10 +75,17 @@ def code_hash(lib=None):
     return hashlib.sha256(sec).hexdigest()[:16]
 
 
+# a kernel of this library (namespace mo, mangled or not); other kernels (torch's
+# input generation, runtime copies) are left out of the summaries
+_OWN = re.compile(r"(_ZN2mo|\bmo::)")
+
+
 def kind_of(name):
     for pat, kind in KINDS:
         if pat.search(name):
             return kind
+    if _OWN.search(name):
+        raise ValueError(f"library kernel of no known kind: {name!r}")
     return None
 
 

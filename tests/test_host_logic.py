@@ -122,6 +122,26 @@ def test_profsummary_kind_names():
         assert kind in bench_kinds()
 
 
+def test_profsummary_classifies_every_kernel_of_the_built_library():
+    """Every kernel in the library's GPU code objects (its `<symbol>.kd` descriptors,
+    each template instantiation included) maps to a kind, and the text rocprofv3's
+    demangler makes of one bf16 instantiation is refused rather than dropped."""
+    import re
+    from matrix_optimizers_sharded_amd import binding
+    path = binding.library_path()
+    if not os.path.exists(path):
+        pytest.fail("libmatopt.so is not built (python -m matrix_optimizers_sharded_amd.build)")
+    data = open(path, "rb").read()
+    syms = {m.decode() for m in re.findall(rb"(_ZN[0-9A-Za-z_]+)\.kd\0", data)}
+    assert len(syms) > 20
+    kinds = {s: profsummary.kind_of(s) for s in syms}
+    assert all(kinds.values()), [s for s, k in kinds.items() if not k]
+    assert {"ns_syrk", "ns_poly", "ns_apply", "momentum_prep", "sign_vote"} <= set(kinds.values())
+    with pytest.raises(ValueError):
+        profsummary.kind_of("void mo::k_ns_gemm<bool _Accum, int, E, bool _Accum, bool, E>"
+                            "(mo::MatDesc const*, int, long, int, float, float, float, float const*)")
+
+
 def bench_kinds():
     """Kind names the library's per-kernel timing reports (mo_profile_end)."""
     import re
