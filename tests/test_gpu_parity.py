@@ -352,6 +352,46 @@ def test_deterministic_and_batch_invariant(gpu):
         np.testing.assert_array_equal(mi[0].view(np.uint32), m1[i].view(np.uint32))
 
 
+def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
+    """bf16 products of a launch whose matrices all have m <= 2048 run on the kernel's
+    small-matrix instantiation (a diagonal SYRK / POLY tile loads its row panel once
+    and reads both operands from it; APPLY stages its rows through LDS); a launch
+    holding any larger matrix runs the plain one.  Both compute the same sums in the
+    same order, so the small matrices' results must be equal bit for bit whether they
+    run alone or beside a 2304-row matrix.  The no-allocation entry point keeps each
+    call in one launch per product (no two-stream halves), so every matrix of a call
+    shares that call's instantiation."""
+    import torch
+    from matrix_optimizers_sharded_amd import muon_step_batched_noalloc
+    small = [(768, 768), (600, 1000), (1000, 600), (1300, 1800), (2048, 2304)]
+    big = (2304, 2560)
+    shapes = small + [big]
+    grads = [bf16_round(gaussian(s, 1600 + i, 0.02))[1] for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 1700 + i, 0.02) for i, s in enumerate(shapes)]
+
+    def run(idx):
+        g = [to_dev_bf16(f32_to_bf16_bits(grads[i]), gpu) for i in idx]
+        m = [to_dev_f32(moms[i], gpu) for i in idx]
+        o = [torch.empty(shapes[i], dtype=torch.bfloat16, device=gpu) for i in idx]
+        torch.cuda.synchronize()
+        muon_step_batched_noalloc(g, m, o, BETA, *MUON_ABC, 5, EPS, compute=torch.bfloat16)
+        torch.cuda.synchronize()
+        return [host_f32(x) for x in m], [host_f32(x) for x in o]
+
+    say("small-matrix kernel: the small set alone, then beside a 2304-row matrix")
+    m_small, u_small = run(range(len(small)))
+    m_mixed, u_mixed = run(range(len(shapes)))
+    for i, sh in enumerate(small):
+        np.testing.assert_array_equal(u_small[i].view(np.uint32), u_mixed[i].view(np.uint32),
+                                      err_msg=f"U of {sh}")
+        np.testing.assert_array_equal(m_small[i].view(np.uint32), m_mixed[i].view(np.uint32),
+                                      err_msg=f"momentum of {sh}")
+    # and the small-matrix kernel's results stay within the oracle's bar
+    few = [0, 1, 2]
+    check_muon([grads[i] for i in few], [moms[i] for i in few], [m_small[i] for i in few],
+               [u_small[i] for i in few], "bf16", MUON_ABC, 5, label="small-matrix kernel")
+
+
 def test_split_batch_follows_the_callers_stream(gpu):
     """A batch with few rounds of tiles per launch runs its products as two halves,
     one on the caller's stream and one on the library's second stream.  Inputs
