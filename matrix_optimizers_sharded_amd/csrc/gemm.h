@@ -345,9 +345,10 @@ struct TileRef {
 // SMALLK (bf16 operands only) is chosen by the host for launches whose matrices all
 // have m <= 2048, where a tile holds at most 32 k-slabs and its fixed costs weigh
 // more: a diagonal SYRK / POLY tile, whose two operands are the same row panel,
-// loads that panel once and reads both operands' fragments from it, and APPLY sends
-// its rows out through the epilogue staging slab as whole 1 KiB runs.  Both were
-// measured slower at the 7B-class set (m = 4096), which keeps the plain kernel.
+// loads that panel once and reads both operands' fragments from it, and APPLY (and
+// SYRK off the diagonal) sends its rows out through the epilogue staging slab as
+// whole 1 KiB runs.  The first two were measured slower at the 7B-class set
+// (m = 4096), which keeps the plain kernel.
 constexpr int SMALLK_MAX_M = 2048;
 template <typename T, int MODE, typename TO, bool SMALLK = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
@@ -761,34 +762,38 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           return e;
         };
         unsigned char* stg = staging + wave * 4096;
-        if constexpr (SMALLK && MODE == GM_APPLY) {
-          // X' through the staging slab: the wave's 64 columns are one 128-byte
-          // k-block row, so a round of 32 rows (one MFMA row block) goes out as 4
-          // stores of 8 whole rows (1 KiB contiguous) each
+        // One row block (32 rows) of row-major results through the staging slab: the
+        // wave's 64 columns are one 128-byte k-block row, so the block goes out as 4
+        // stores of 8 whole rows (1 KiB contiguous) each, not 64 stores of 128 bytes.
+        // The small-matrix kernel does this for APPLY's X' and for SYRK's A off the
+        // diagonal (whose rows are stored whole).
+        auto stage_rows = [&](int a) {
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
+          for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
-              for (int g = 0; g < 4; ++g)
+              for (int t = 0; t < 4; ++t) {
+                const int r = 8 * g + 4 * half + t;        // row within the block
+                const int off = (b * 32 + l32) * 2;        // byte within the row
+                *reinterpret_cast<T*>(stg + r * 128 + ((((off >> 4) ^ (r & 7)) << 4) | (off & 15))) =
+                    from_f32<T>(acc[a][b][4 * g + t] * alpha);
+              }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const int r = 8 * g + 4 * half + t;        // row within the round
-                  const int off = (b * 32 + l32) * 2;        // byte within the row
-                  *reinterpret_cast<T*>(stg + r * 128 + ((((off >> 4) ^ (r & 7)) << 4) | (off & 15))) =
-                      from_f32<T>(acc[a][b][4 * g + t] * alpha);
-                }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = (lane >> 3) + 8 * q, c = lane & 7;
-              const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ (r & 7)) << 4));
-              store_ws(at<u32x4_t>(Cr, kb_off<T>(i0 + wm + a * 32 + r, j0 + wn + c * 8, pr)), w);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // rounds one after another
+          for (int q = 0; q < 4; ++q) {
+            const int r = (lane >> 3) + 8 * q, c = lane & 7;
+            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ (r & 7)) << 4));
+            store_ws(at<u32x4_t>(Cr, kb_off<T>(i0 + wm + a * 32 + r, j0 + wn + c * 8, pr)), w);
           }
+          __builtin_amdgcn_sched_barrier(0);   // blocks one after another
+        };
+        const bool staged_rows = SMALLK && MODE == GM_SYRK && !diag;
+        if constexpr (SMALLK && MODE == GM_APPLY) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) stage_rows(a);
         } else
 #pragma unroll
-        for (int p = 0; p < 4 / AP; ++p)
+        for (int p = 0; p < 4 / AP; ++p) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const int j = j0 + wn + b * 32 + l32;
@@ -809,7 +814,9 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
                 values(a, b, g, ib, j, e[ap][g], v);
                 // rows ib..ib+3 of column j: consecutive rows of one k-block are
                 // ROW_BYTES apart, and a half-wave writes 64 contiguous bytes per row
-                if (MODE == GM_POLY && !diag) {
+                if (staged_rows) {
+                  // stored whole after this pair of row blocks' mirror rounds
+                } else if (MODE == GM_POLY && !diag) {
                   store_pairs<T>(Cr, pr, lane, ib, j, v);
                 } else {
                   const uint32_t o = kb_off<T>(ib, j, pr);
@@ -849,6 +856,11 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             }
             __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
           }
+          if constexpr (SMALLK && MODE == GM_SYRK) if (staged_rows) {
+#pragma unroll
+            for (int ap = 0; ap < AP; ++ap) stage_rows(AP * p + ap);
+          }
+        }
       } else {
         const gptr<TO> out = global(static_cast<TO*>(d.out));
         const int m = d.m, n = d.n;
