@@ -345,9 +345,9 @@ struct TileRef {
 // SMALLK (bf16 operands only) is chosen by the host for launches whose matrices all
 // have m <= 2048, where a tile holds at most 32 k-slabs and its fixed costs weigh
 // more: a diagonal SYRK / POLY tile, whose two operands are the same row panel,
-// loads that panel once and reads both operands' fragments from it, and APPLY (and
-// SYRK off the diagonal) sends its rows out through the epilogue staging slab as
-// whole 1 KiB runs.  The first two were measured slower at the 7B-class set
+// loads that panel once and reads both operands' fragments from it, and APPLY sends
+// its rows out through the epilogue staging slab as whole 1 KiB runs (as SYRK does
+// off the diagonal in both kernels).  Both were measured slower at the 7B-class set
 // (m = 4096), which keeps the plain kernel.
 constexpr int SMALLK_MAX_M = 2048;
 template <typename T, int MODE, typename TO, bool SMALLK = false>
@@ -764,9 +764,10 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         unsigned char* stg = staging + wave * 4096;
         // One row block (32 rows) of row-major results through the staging slab: the
         // wave's 64 columns are one 128-byte k-block row, so the block goes out as 4
-        // stores of 8 whole rows (1 KiB contiguous) each, not 64 stores of 128 bytes.
-        // The small-matrix kernel does this for APPLY's X' and for SYRK's A off the
-        // diagonal (whose rows are stored whole).
+        // stores of 8 whole rows (1 KiB contiguous) each, not 64 stores of 128 bytes
+        // (bf16 only: a row of 64 fp32 values spans two k-blocks).  Used for SYRK's A
+        // off the diagonal (whose rows are stored whole), and in the small-matrix
+        // kernel for APPLY's X'.
         auto stage_rows = [&](int a) {
 #pragma unroll
           for (int b = 0; b < NB; ++b)
@@ -787,7 +788,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           }
           __builtin_amdgcn_sched_barrier(0);   // blocks one after another
         };
-        const bool staged_rows = SMALLK && MODE == GM_SYRK && !diag;
+        const bool staged_rows = MODE == GM_SYRK && sizeof(T) == 2 && !diag;
         if constexpr (SMALLK && MODE == GM_APPLY) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) stage_rows(a);
@@ -856,7 +857,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
             }
             __builtin_amdgcn_sched_barrier(0);   // rounds one after another: bounded live ranges
           }
-          if constexpr (SMALLK && MODE == GM_SYRK) if (staged_rows) {
+          if constexpr (MODE == GM_SYRK && sizeof(T) == 2) if (staged_rows) {
 #pragma unroll
             for (int ap = 0; ap < AP; ++ap) stage_rows(AP * p + ap);
           }
