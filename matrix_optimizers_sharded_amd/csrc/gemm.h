@@ -345,10 +345,8 @@ struct TileRef {
 // SMALLK (bf16 operands only) is chosen by the host for launches whose matrices all
 // have m <= 2048, where a tile holds at most 32 k-slabs and its fixed costs weigh
 // more: a diagonal SYRK / POLY tile, whose two operands are the same row panel,
-// loads that panel once and reads both operands' fragments from it, and APPLY sends
-// its rows out through the epilogue staging slab as whole 1 KiB runs (as SYRK does
-// off the diagonal in both kernels).  Both were measured slower at the 7B-class set
-// (m = 4096), which keeps the plain kernel.
+// loads that panel once and reads both operands' fragments from it.  That was
+// measured slower at the 7B-class set (m = 4096), which keeps the plain kernel.
 constexpr int SMALLK_MAX_M = 2048;
 template <typename T, int MODE, typename TO, bool SMALLK = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
@@ -765,9 +763,8 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
         // One row block (32 rows) of row-major results through the staging slab: the
         // wave's 64 columns are one 128-byte k-block row, so the block goes out as 4
         // stores of 8 whole rows (1 KiB contiguous) each, not 64 stores of 128 bytes
-        // (bf16 only: a row of 64 fp32 values spans two k-blocks).  Used for SYRK's A
-        // off the diagonal (whose rows are stored whole), and in the small-matrix
-        // kernel for APPLY's X'.
+        // (bf16 only: a row of 64 fp32 values spans two k-blocks).  Used for APPLY's
+        // X' and for SYRK's A off the diagonal (whose rows are stored whole).
         auto stage_rows = [&](int a) {
 #pragma unroll
           for (int b = 0; b < NB; ++b)
@@ -789,7 +786,7 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
           __builtin_amdgcn_sched_barrier(0);   // blocks one after another
         };
         const bool staged_rows = MODE == GM_SYRK && sizeof(T) == 2 && !diag;
-        if constexpr (SMALLK && MODE == GM_APPLY) {
+        if constexpr (sizeof(T) == 2 && MODE == GM_APPLY) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) stage_rows(a);
         } else

@@ -380,7 +380,7 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
     int count;
     int64_t ts, tp, ta;
     hipStream_t stream;
-    bool smallk;   // bf16 operands and every matrix m <= SMALLK_MAX_M (gemm.h)
+    bool smallk;   // SYRK / POLY: bf16 operands and every matrix m <= SMALLK_MAX_M (gemm.h)
   };
   Half halves[2];
   int nh = 1;
@@ -400,7 +400,7 @@ int run_ns(const MatDesc* dd, int count, const Plan& plan, const mo_ns_params& n
                   const float* f) {
     constexpr int M = decltype(mode)::value;
     const dim3 grid(gemm_grid(items));
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && (M == GM_SYRK || M == GM_POLY)) {
       if (H.smallk) {
         hipLaunchKernelGGL((k_ns_gemm<T, M, TO, true>), grid, dim3(NTHREADS), 0, H.stream, H.dd, H.count, items,
                            parity, ca, cb, cc, f);

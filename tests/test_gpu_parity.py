@@ -353,10 +353,9 @@ def test_deterministic_and_batch_invariant(gpu):
 
 
 def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
-    """bf16 products of a launch whose matrices all have m <= 2048 run on the kernel's
-    small-matrix instantiation (a diagonal SYRK / POLY tile loads its row panel once
-    and reads both operands from it; APPLY stages its rows through LDS); a launch
-    holding any larger matrix runs the plain one.  Both compute the same sums in the
+    """bf16 SYRK / POLY launches whose matrices all have m <= 2048 run on the kernel's
+    small-matrix instantiation (a diagonal tile loads its row panel once and reads
+    both operands from it); a launch holding any larger matrix runs the plain one.  Both compute the same sums in the
     same order, so the small matrices' results must be equal bit for bit whether they
     run alone or beside a 2304-row matrix.  The no-allocation entry point keeps each
     call in one launch per product (no two-stream halves), so every matrix of a call
