@@ -357,13 +357,15 @@ def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
     small-matrix instantiation (a diagonal tile loads its row panel once and reads
     both operands from it); a launch holding any larger matrix runs the plain one.  Both compute the same sums in the
     same order, so the small matrices' results must be equal bit for bit whether they
-    run alone or beside a 2304-row matrix.  The no-allocation entry point keeps each
+    run alone or beside a 2100-row matrix.  The no-allocation entry point keeps each
     call in one launch per product (no two-stream halves), so every matrix of a call
-    shares that call's instantiation."""
+    shares that call's instantiation.  The large matrix is ragged (2100 x 2700: the
+    last tile row and column are partial), so the plain kernel's edge tiles are
+    checked against the oracle as well."""
     import torch
     from matrix_optimizers_sharded_amd import muon_step_batched_noalloc
     small = [(768, 768), (600, 1000), (1000, 600), (1300, 1800), (2048, 2304)]
-    big = (2304, 2560)
+    big = (2100, 2700)
     shapes = small + [big]
     grads = [bf16_round(gaussian(s, 1600 + i, 0.02))[1] for i, s in enumerate(shapes)]
     moms = [gaussian(s, 1700 + i, 0.02) for i, s in enumerate(shapes)]
@@ -377,7 +379,7 @@ def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
         torch.cuda.synchronize()
         return [host_f32(x) for x in m], [host_f32(x) for x in o]
 
-    say("small-matrix kernel: the small set alone, then beside a 2304-row matrix")
+    say("small-matrix kernel: the small set alone, then beside a ragged 2100-row matrix")
     m_small, u_small = run(range(len(small)))
     m_mixed, u_mixed = run(range(len(shapes)))
     for i, sh in enumerate(small):
@@ -389,6 +391,9 @@ def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
     few = [0, 1, 2]
     check_muon([grads[i] for i in few], [moms[i] for i in few], [m_small[i] for i in few],
                [u_small[i] for i in few], "bf16", MUON_ABC, 5, label="small-matrix kernel")
+    k = len(small)
+    check_muon([grads[k]], [moms[k]], [m_mixed[k]], [u_mixed[k]], "bf16", MUON_ABC, 5,
+               label="plain kernel, ragged 2100 x 2700")
 
 
 def test_split_batch_follows_the_callers_stream(gpu):
