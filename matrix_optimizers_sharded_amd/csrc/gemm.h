@@ -709,8 +709,11 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       // ib..ib+3 of one column j per register group g.
       //
       // Both destinations are k-blocked along their columns (a 128-byte k-block row is
-      // one line).  Row-major results (X', or C = A or B') are stored straight from the
-      // registers: one instruction writes 64 contiguous bytes of each of 2 rows.  The
+      // one line).  Row-major results straight from the registers take one instruction
+      // per 64 contiguous bytes of each of 2 rows; with bf16 operands, APPLY's X' and
+      // SYRK's off-diagonal A go through the staging slab below and leave as whole
+      // lines instead (POLY has no registers to spare for that and stores its B'
+      // tile's rows as 2-column pieces).  The
       // mirror tile of C (SYRK and POLY) would leave the registers as 8 or 16 bytes per
       // row per instruction, i.e. 8 partial writes per line, and L2 write traffic of
       // that shape slows everyone's operand loads.  It goes through this wave's 4 KiB
