@@ -342,12 +342,12 @@ struct TileRef {
 // slabs of a tile start the loads of the next tile's first slabs, so those land while
 // this tile finishes and writes its epilogue, and no tile pays a cold start.  (A
 // shared work queue fed by an atomic counter measured about 1% slower.)
-// SMALLK (bf16 operands only) is chosen by the host for launches whose matrices all
-// have m <= 1024, where a tile holds at most 16 k-slabs and its fixed costs weigh
-// more: a diagonal SYRK / POLY tile, whose two operands are the same row panel,
-// loads that panel once and reads both operands' fragments from it.  That was
-// measured slower at the 1B- and 7B-class sets (m = 2048 and 4096), which keep the
-// plain kernel.
+// SMALLK (bf16 operands only) is chosen by the host for SYRK / POLY launches whose
+// matrices all have m <= 1024: at most 4 x 4 tiles per matrix, two fifths or more of
+// the upper ones diagonal, and POLY tiles of at most 16 k-slabs.  A diagonal tile,
+// whose two operands are the same row panel, loads that panel once and reads both
+// operands' fragments from it.  That was measured slower at the 1B- and 7B-class
+// sets (m = 2048 and 4096), which keep the plain kernel.
 constexpr int SMALLK_MAX_M = 1024;
 template <typename T, int MODE, typename TO, bool SMALLK = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(NWAVES / 4, NWAVES / 4)))
