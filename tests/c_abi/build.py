@@ -28,5 +28,39 @@ def build(verbose=False):
     return BIN
 
 
+ASAN_SRC = os.path.join(HERE, "asan_host.cpp")
+ASAN_LIB = os.path.join(HERE, "libmatopt_asan.so")
+ASAN_BIN = os.path.join(HERE, "asan_host")
+HOST_CLANG = os.environ.get("HOST_CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def build_asan(verbose=False):
+    """A debug build of libmatopt.so whose host code (the C ABI, argument checks,
+    planning, the planner) carries AddressSanitizer, and tests/c_abi/asan_host, a
+    host-only program linked against it and built with the same compiler's
+    sanitizer runtime.  Device code is built as usual; the sanitizer is asked for on
+    the host side only."""
+    src = os.path.join(ROOT, "matrix_optimizers_sharded_amd", "csrc", "matopt.hip")
+    lib_cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+               "-I", os.path.join(ROOT, "include"), "-o", ASAN_LIB + ".tmp", src]
+    bin_cmd = [HOST_CLANG, "-O1", "-g", "-std=c++17", "-fsanitize=address", "-fno-omit-frame-pointer",
+               "-I", os.path.join(ROOT, "include"), ASAN_SRC, "-L", HERE, "-lmatopt_asan",
+               "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib", "-L/opt/rocm/lib", "-lamdhip64",
+               "-o", ASAN_BIN + ".tmp"]
+    for cmd, tmp, final in ((lib_cmd, ASAN_LIB + ".tmp", ASAN_LIB), (bin_cmd, ASAN_BIN + ".tmp", ASAN_BIN)):
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"building {os.path.basename(final)} failed")
+        os.replace(tmp, final)
+    if verbose:
+        print(f"built {ASAN_LIB} and {ASAN_BIN}")
+    return ASAN_BIN
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    if "--asan" in sys.argv:
+        build_asan(verbose=True)
