@@ -866,48 +866,118 @@ void k_ns_gemm(const MatDesc* __restrict__ descs, int count, int64_t total, int 
       } else {
         const gptr<TO> out = global(static_cast<TO*>(d.out));
         const int m = d.m, n = d.n;
+        // register group (a, b, g): rows ib..ib+3 of column j, element by element
+        // (or 4 at a time along a transposed output's row)
+        auto plain_group = [&](int a, int b, int g) {
+          const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
+          const int j = j0 + wn + b * 32 + l32;
+          float v[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+          for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t] * alpha;
+          // the value stored at o: U itself, or W - lr * U
+          auto result = [&](gptr<TO> o, float u) {
+            return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);
+          };
+          if (j < n) {
+            if (!d.transposed) {
+              // out is m x n row-major
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int ib = i0 + wm + a * 32 + 8 * g + 4 * half;
-              const int j = j0 + wn + b * 32 + l32;
-              float v[4];
-#pragma unroll
-              for (int t = 0; t < 4; ++t) v[t] = acc[a][b][4 * g + t] * alpha;
-              // the value stored at o: U itself, or W - lr * U
-              auto result = [&](gptr<TO> o, float u) {
-                return from_f32<TO>(MODE == GM_APPLY_WEIGHT ? to_f32(*o) - ca * u : u);
-              };
-              if (j < n) {
-                if (!d.transposed) {
-                  // out is m x n row-major
-#pragma unroll
-                  for (int t = 0; t < 4; ++t)
-                    if (ib + t < m) {
-                      const gptr<TO> o = out + static_cast<int64_t>(ib + t) * n + j;
-                      *o = result(o, v[t]);
-                    }
-                } else {
-                  // out is n x m row-major: out[j][i]
-                  const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
-                  if (d.vec_ok && ib + 4 <= m) {
-                    if (MODE == GM_APPLY_WEIGHT) {
-                      typedef typename Vec4<TO>::type w4_t;
-                      const w4_t w = *reinterpret_cast<gptr<const w4_t>>(o);
-#pragma unroll
-                      for (int t = 0; t < 4; ++t) v[t] = to_f32(w[t]) - ca * v[t];
-                    }
-                    store4<TO>(o, v[0], v[1], v[2], v[3]);
-                  } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                      if (ib + t < m) o[t] = result(o + t, v[t]);
-                  }
+              for (int t = 0; t < 4; ++t)
+                if (ib + t < m) {
+                  const gptr<TO> o = out + static_cast<int64_t>(ib + t) * n + j;
+                  *o = result(o, v[t]);
                 }
+            } else {
+              // out is n x m row-major: out[j][i]
+              const gptr<TO> o = out + static_cast<int64_t>(j) * m + ib;
+              if (d.vec_ok && ib + 4 <= m) {
+                if (MODE == GM_APPLY_WEIGHT) {
+                  typedef typename Vec4<TO>::type w4_t;
+                  const w4_t w = *reinterpret_cast<gptr<const w4_t>>(o);
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) v[t] = to_f32(w[t]) - ca * v[t];
+                }
+                store4<TO>(o, v[0], v[1], v[2], v[3]);
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (ib + t < m) o[t] = result(o + t, v[t]);
               }
+            }
+          }
+        };
+        // U with bf16 elements through the staging slab, for blocks wholly inside the
+        // matrix: whole 128-byte pieces of U's rows (64 elements) instead of 2-byte
+        // stores (U as stored) or 8-byte pieces spread over 64 rows (U transposed).
+        // Needs 16-byte aligned rows: the output base (vec_ok) and the row pitch.
+        unsigned char* stg = staging + wave * 4096;
+        const bool stage_out = MODE == GM_APPLY_FINAL && sizeof(TO) == 2 && d.vec_ok &&
+                               (static_cast<int64_t>(d.transposed ? m : n) * 2) % 16 == 0;
+        if (!d.transposed) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int r0 = i0 + wm + a * 32;
+            if (sizeof(TO) == 2 && stage_out && r0 + 32 <= m && j0 + wn + 64 <= n) {
+              // rows r0..r0+31, columns j0+wn..+63: [row][column] in the slab
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) {
+                    const int r = 8 * g + 4 * half + t;
+                    const int off = (b * 32 + l32) * 2;
+                    *reinterpret_cast<TO*>(stg + r * 128 + ((((off >> 4) ^ (r & 7)) << 4) | (off & 15))) =
+                        from_f32<TO>(acc[a][b][4 * g + t] * alpha);
+                  }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int r = (lane >> 3) + 8 * q, c = lane & 7;
+                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ (r & 7)) << 4));
+                *reinterpret_cast<gptr<u32x4_t>>(out + static_cast<int64_t>(r0 + r) * n + j0 + wn + c * 8) = w;
+              }
+            } else {
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) plain_group(a, b, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // blocks one after another
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const int ir = i0 + wm + 64 * p, jc = j0 + wn + b * 32;
+              if (sizeof(TO) == 2 && stage_out && ir + 64 <= m && jc + 32 <= n) {
+                // columns jc..jc+31 as rows of U, rows ir..ir+63 of X' along them:
+                // [j][i] in the slab
+                typedef typename Vec4<TO>::type o4_t;
+#pragma unroll
+                for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+                  for (int g = 0; g < 4; ++g) {
+                    const int a = 2 * p + ap;
+                    const o4_t w = {from_f32<TO>(acc[a][b][4 * g] * alpha), from_f32<TO>(acc[a][b][4 * g + 1] * alpha),
+                                    from_f32<TO>(acc[a][b][4 * g + 2] * alpha),
+                                    from_f32<TO>(acc[a][b][4 * g + 3] * alpha)};
+                    const int off = (32 * ap + 8 * g + 4 * half) * 2;
+                    *reinterpret_cast<o4_t*>(stg + l32 * 128 + ((((off >> 4) ^ (l32 & 7)) << 4) | (off & 15))) = w;
+                  }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int jr = (lane >> 3) + 8 * r, c = lane & 7;
+                  const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + jr * 128 + ((c ^ (jr & 7)) << 4));
+                  *reinterpret_cast<gptr<u32x4_t>>(out + static_cast<int64_t>(jc + jr) * m + ir + c * 8) = w;
+                }
+              } else {
+#pragma unroll
+                for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+                  for (int g = 0; g < 4; ++g) plain_group(2 * p + ap, b, g);
+              }
+              __builtin_amdgcn_sched_barrier(0);   // rounds one after another
             }
         }
       }
