@@ -396,6 +396,36 @@ def test_small_matrix_kernel_equals_the_plain_kernel(gpu):
                label="plain kernel, ragged 2100 x 2700")
 
 
+def test_staged_output_with_edge_tiles(gpu):
+    """The last product writes bf16 U through LDS as whole row pieces on blocks wholly
+    inside the matrix when U's rows are 16-byte aligned, and element by element
+    elsewhere.  These shapes have aligned rows (cols a multiple of 8) but sizes off
+    the 256 grid, so one matrix mixes both paths, untransposed (wide) and transposed
+    (tall); two more have rows only 8-byte aligned, which take the element path
+    throughout."""
+    import torch
+    shapes = [(1000, 1288), (1288, 1000), (520, 2056), (2056, 520), (776, 1004), (1004, 772)]
+    grads = [bf16_round(gaussian(s, 1800 + i, 0.02))[1] for i, s in enumerate(shapes)]
+    moms = [gaussian(s, 1900 + i, 0.02) for i, s in enumerate(shapes)]
+    say("staged U with edge tiles: " + ", ".join(f"{r}x{c}" for r, c in shapes))
+    gm, gu = run_muon(gpu, grads, moms, torch.bfloat16, torch.bfloat16, torch.bfloat16, BETA, MUON_ABC, 5, EPS)
+    check_muon(grads, moms, gm, gu, "bf16", MUON_ABC, 5, label="staged U, edge tiles")
+    # the same U written one element off 16-byte alignment takes the element path
+    # everywhere: both paths round the same values, so U must be equal bit for bit
+    from matrix_optimizers_sharded_amd import muon_step_batched
+    g_dev = [to_dev_bf16(f32_to_bf16_bits(g), gpu) for g in grads]
+    m_dev = [to_dev_f32(m, gpu) for m in moms]
+    flat = [torch.empty(r * c + 8, dtype=torch.bfloat16, device=gpu) for r, c in shapes]
+    outs = [f[1:1 + r * c].view(r, c) for f, (r, c) in zip(flat, shapes)]
+    assert all(o.data_ptr() % 16 != 0 for o in outs)
+    torch.cuda.synchronize()
+    muon_step_batched(g_dev, m_dev, outs, BETA, *MUON_ABC, 5, EPS, compute=torch.bfloat16)
+    torch.cuda.synchronize()
+    for i, sh in enumerate(shapes):
+        np.testing.assert_array_equal(host_f32(outs[i]).view(np.uint32), gu[i].view(np.uint32),
+                                      err_msg=f"U of {sh}: staged against element by element")
+
+
 def test_split_batch_follows_the_callers_stream(gpu):
     """A batch with few rounds of tiles per launch runs its products as two halves,
     one on the caller's stream and one on the library's second stream.  Inputs
